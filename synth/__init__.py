@@ -1,0 +1,203 @@
+"""Seeded synthetic inputs for the tiled GEMM/BMM workloads.
+
+This module only draws random numbers and encodes them as 16-bit floating
+point bit patterns.  It holds none of the matrix-multiply arithmetic: both the
+HIP path (through the tests and the benchmark) and the CPU oracle receive the
+very same arrays from here, and neither side's code lives here.
+
+Recipe (the pages fix no generator, seed layout or encoding; these are the
+readings this project takes):
+
+* ``numpy.random.default_rng(seed)`` (PCG64).  Each array is drawn whole, in
+  C order, in the order its workload lists it; large arrays are drawn in
+  contiguous chunks, which yields the same stream as one draw.
+* Uniform on [lo, hi): ``lo + (hi - lo) * rng.random()``.  Normal with
+  standard deviation s: ``s * rng.standard_normal()``.
+* float64 draws are rounded to float32 (round-to-nearest-even) and then to
+  bf16 by round-to-nearest-even using torch's own conversion; fp16 inputs are
+  rounded from float64 by numpy's conversion.  Rounding may turn a value just
+  below ``hi`` into ``hi``; tolerances use the observed maxima, so this is
+  harmless.
+
+The workloads are the GEMM shapes the pages tune for (square, ragged, tall-thin
+inference) and the two batched products of an attention head
+(p1 "Triton Optimization Reference", intro and section 3; p2 "Optimize Triton
+Block Parameters", Performance requirements, shape-specific tuning).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Tuple
+
+import numpy as np
+
+_CHUNK = 1 << 22  # elements per draw; any value gives the same stream
+
+
+def _f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _encode(x64: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return _f32_to_bf16_bits(x64.astype(np.float32))
+    if dtype == "fp16":
+        return x64.astype(np.float16).view(np.uint16)
+    raise ValueError(f"unknown input dtype {dtype!r}")
+
+
+def draw(rng: np.random.Generator, shape, dist: str, a: float, b: float = 0.0,
+         dtype: str = "bf16") -> np.ndarray:
+    """Draw an array of 16-bit float bit patterns (uint16) of ``shape``.
+
+    ``dist`` is "uniform" (on [a, b)), "normal" (std a) or "int" (integers in
+    [a, b], inclusive, exactly representable).
+    """
+    shape = tuple(int(s) for s in shape)
+    n = int(np.prod(shape, dtype=np.int64))
+    out = np.empty(n, dtype=np.uint16)
+    for lo in range(0, n, _CHUNK):
+        cnt = min(_CHUNK, n - lo)
+        if dist == "uniform":
+            x = a + (b - a) * rng.random(cnt)
+        elif dist == "normal":
+            x = a * rng.standard_normal(cnt)
+        elif dist == "int":
+            x = rng.integers(int(a), int(b) + 1, size=cnt).astype(np.float64)
+        else:
+            raise ValueError(f"unknown distribution {dist!r}")
+        out[lo:lo + cnt] = _encode(x, dtype)
+    return out.reshape(shape)
+
+
+def bits_to_float(bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """Widen bit patterns to float32 (for host-side inspection only)."""
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << 16).view(np.float32)
+    return bits.view(np.float16).astype(np.float32)
+
+
+@dataclasses.dataclass
+class Problem:
+    """One GEMM or BMM call: C[b] = op(A[b]) @ op(B[b]) with row-major storage."""
+    name: str
+    A: np.ndarray                 # uint16 bit patterns, stored shape
+    B: np.ndarray
+    trans_a: int
+    trans_b: int
+    m: int
+    n: int
+    k: int
+    batch: int = 1
+    in_dtype: str = "bf16"
+    out_dtype: str = "fp32"
+    lda: int = 0
+    ldb: int = 0
+    ldc: int = 0
+    stride_a: int = 0
+    stride_b: int = 0
+    stride_c: int = 0
+
+    def __post_init__(self):
+        if not self.lda:
+            self.lda = self.m if self.trans_a else self.k
+        if not self.ldb:
+            self.ldb = self.k if self.trans_b else self.n
+        if not self.ldc:
+            self.ldc = self.n
+        if self.batch > 1:
+            if not self.stride_a:
+                self.stride_a = (self.k if self.trans_a else self.m) * self.lda
+            if not self.stride_b:
+                self.stride_b = (self.n if self.trans_b else self.k) * self.ldb
+            if not self.stride_c:
+                self.stride_c = self.m * self.ldc
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.m * self.n * self.k * self.batch
+
+
+# ---------------------------------------------------------------------------
+# The five workloads.  Sizes, distributions and seeds are the ones the
+# project's benchmark configurations name; layouts follow the readings listed
+# in the design notes (row-major op letters; NT = B stored N x K).
+# ---------------------------------------------------------------------------
+
+def square_256(seed: int = 0) -> List[Problem]:
+    rng = np.random.default_rng(seed)
+    A = draw(rng, (256, 256), "uniform", -1.0, 1.0)
+    B = draw(rng, (256, 256), "uniform", -1.0, 1.0)
+    return [Problem("square_256_nn", A, B, 0, 0, 256, 256, 256)]
+
+
+def ragged_1000(seed: int = 1) -> List[Problem]:
+    """The same two stored 1000x1000 arrays read under all four transposes."""
+    rng = np.random.default_rng(seed)
+    A = draw(rng, (1000, 1000), "uniform", -1.0, 1.0)
+    B = draw(rng, (1000, 1000), "uniform", -1.0, 1.0)
+    out = []
+    for ta in (0, 1):
+        for tb in (0, 1):
+            tag = ("T" if ta else "N") + ("T" if tb else "N")
+            out.append(Problem(f"ragged_1000_{tag.lower()}", A, B, ta, tb, 1000, 1000, 1000))
+    return out
+
+
+def skinny_16(seed: int = 2, out_dtype: str = "bf16") -> List[Problem]:
+    """M=16 activations against an N x K weight matrix (B stored N x K)."""
+    rng = np.random.default_rng(seed)
+    A = draw(rng, (16, 8192), "normal", 1.0)
+    B = draw(rng, (8192, 8192), "normal", 0.02)
+    return [Problem("skinny_16x8192x8192_nt", A, B, 0, 1, 16, 8192, 8192, out_dtype=out_dtype)]
+
+
+def attention_bmm(seed: int = 3, batch: int = 128, seq: int = 2048, head: int = 128) -> List[Problem]:
+    """S = Q K^T and O = P V for ``batch`` heads; P is independent synthetic data."""
+    rng = np.random.default_rng(seed)
+    Q = draw(rng, (batch, seq, head), "normal", 1.0)
+    K = draw(rng, (batch, seq, head), "normal", 1.0)
+    P = draw(rng, (batch, seq, seq), "uniform", 0.0, 1.0 / 2048.0)
+    V = draw(rng, (batch, seq, head), "normal", 1.0)
+    s = Problem(f"attn_s_b{batch}_{seq}x{seq}x{head}_nt", Q, K, 0, 1, seq, seq, head, batch=batch)
+    o = Problem(f"attn_o_b{batch}_{seq}x{head}x{seq}_nn", P, V, 0, 0, seq, head, seq, batch=batch)
+    return [s, o]
+
+
+def square_8192(seed: int = 4, out_dtype: str = "bf16") -> List[Problem]:
+    rng = np.random.default_rng(seed)
+    A = draw(rng, (8192, 8192), "normal", 1.0)
+    B = draw(rng, (8192, 8192), "normal", 1.0)
+    return [Problem("square_8192_nn", A, B, 0, 0, 8192, 8192, 8192, out_dtype=out_dtype)]
+
+
+WORKLOADS = {
+    "square_256": square_256,
+    "ragged_1000": ragged_1000,
+    "skinny_16": skinny_16,
+    "attention_bmm": attention_bmm,
+    "square_8192": square_8192,
+}
+
+
+def sample_indices(seed: int, batch: int, m: int, n: int, count: int = 4096,
+                   edges: Tuple[int, ...] = (0, 63, 64, 127, 128, 255, 256)) -> np.ndarray:
+    """Seeded (b, i, j) triples: ``count`` uniform draws plus tile-edge points.
+
+    Edge points are every pair of {edges, M-1} x {edges, N-1} (clipped to the
+    matrix) in the first and last batch.
+    """
+    rng = np.random.default_rng(1000 + seed)
+    b = rng.integers(0, batch, size=count)
+    i = rng.integers(0, m, size=count)
+    j = rng.integers(0, n, size=count)
+    ei = sorted({e for e in edges if e < m} | {m - 1}) if m else []
+    ej = sorted({e for e in edges if e < n} | {n - 1}) if n else []
+    extra = [(bb, ii, jj) for bb in sorted({0, batch - 1}) for ii in ei for jj in ej]
+    tri = np.stack([b, i, j], axis=1).astype(np.int64)
+    if extra:
+        tri = np.concatenate([tri, np.asarray(extra, dtype=np.int64)], axis=0)
+    return np.ascontiguousarray(tri)
