@@ -1,0 +1,138 @@
+/*
+ * tgemm.h -- tiled bf16/fp16 GEMM and batched GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * Operation (row-major storage throughout):
+ *     C[b] = op(A[b]) * op(B[b])        b = 0 .. batch-1
+ * op(X) is X or its transpose.  The product of op(A) (M x K) and op(B) (K x N)
+ * is the dense matrix multiply whose 2*M*N*K flops and
+ * 2*(M*K + K*N + M*N)-byte footprint the page "Optimize Triton Block
+ * Parameters" (Step 1) uses to place a kernel on the roofline.  A transpose is
+ * expressed only through the addresses used to read the stored operand
+ * ("Triton Optimization Reference", section 2); the batch index only offsets
+ * each operand by its own batch stride (same page, section 3).  Inputs are
+ * bf16 or fp16, products are accumulated in fp32, and the fp32 sum is written
+ * as fp32 or rounded to the input type (round to nearest, ties to even).  C is
+ * overwritten; there is no alpha/beta.
+ *
+ * Storage and leading dimensions (all in elements, all row-major):
+ *   trans_a = 0: A is M x K, element (i,k) at A[i*lda + k],  lda >= max(1, K)
+ *   trans_a = 1: A is stored K x M, op(A)(i,k) = A[k*lda + i], lda >= max(1, M)
+ *   trans_b = 0: B is K x N, element (k,j) at B[k*ldb + j],  ldb >= max(1, N)
+ *   trans_b = 1: B is stored N x K, op(B)(k,j) = B[j*ldb + k], ldb >= max(1, K)
+ *   C is M x N, element (i,j) at C[i*ldc + j],               ldc >= max(1, N)
+ * In batched calls the operands of batch b start at A + b*stride_a,
+ * B + b*stride_b and C + b*stride_c (elements; a stride of 0 reuses one
+ * operand for every batch; C strides must not make batches overlap).
+ *
+ * Ownership: every pointer is caller-owned device memory (A, B, C) or
+ * caller-owned host memory (the plan).  The library allocates nothing, keeps
+ * no global mutable state and is safe to call from several host threads.
+ * C must not alias A or B.
+ *
+ * Errors are returned as tg_status codes; the library never aborts or throws.
+ */
+#ifndef TGEMM_H
+#define TGEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TG_ABI_VERSION 1
+
+typedef enum { TG_BF16 = 0, TG_FP16 = 1, TG_FP32 = 2 } tg_dtype;
+
+typedef enum {
+  TG_OK = 0,
+  TG_ERR_INVALID = 1,     /* bad argument: sizes, leading dims, flags, null pointers, plan */
+  TG_ERR_UNSUPPORTED = 2, /* well-formed but not provided: dtype pair, forced variant/tile */
+  TG_ERR_HIP = 3          /* the HIP runtime rejected the launch */
+} tg_status;
+
+/* Kernel families a plan can select. */
+typedef enum {
+  TG_VARIANT_GENERIC = 0, /* element-wise loads: any alignment and leading dimension */
+  TG_VARIANT_TILE = 1,    /* 16-byte vector loads along each operand's contiguous dim */
+  TG_VARIANT_SKINNY = 2   /* M <= 32, both operands K-contiguous: streams B once */
+} tg_variant;
+
+/* plan.flags bits */
+#define TG_FLAG_EVEN_K 0x1 /* K is a multiple of the K-tile: no masked K step */
+#define TG_FLAG_VEC16 0x2  /* leading dims and contiguous extents allow 16-byte loads */
+
+/*
+ * A plan: caller-owned plain data, filled by gemm_plan(), read by gemm_run()
+ * and bmm_run().  No heap memory behind it and nothing to destroy.  A caller
+ * may overwrite `variant` and `tile` with another supported pair (every pair
+ * gives the same result up to fp32 summation order); the run calls validate
+ * the pair against the problem and return TG_ERR_UNSUPPORTED if it does not fit.
+ */
+typedef struct {
+  int32_t abi_version;          /* TG_ABI_VERSION, set by gemm_plan */
+  int32_t in_type, out_type;    /* tg_dtype */
+  int32_t trans_a, trans_b;     /* 0 or 1 */
+  int64_t m, n, k, lda, ldb, ldc;
+  int32_t variant;              /* tg_variant */
+  int32_t tile;                 /* index into the variant's tile table */
+  int32_t bm, bn, bk;           /* tile shape of (variant, tile), informational */
+  int32_t wg_threads;           /* work-group size */
+  int32_t stages;               /* LDS buffers in the K pipeline */
+  int32_t flags;                /* TG_FLAG_* */
+  uint32_t lds_bytes;           /* LDS per work-group: stages*(bm*bk + bk*bn)*2 */
+  uint32_t reserved0;
+  uint64_t workspace_bytes;     /* always 0: no workspace */
+  int64_t tiles_m, tiles_n;     /* work-groups per matrix = tiles_m * tiles_n */
+} gemm_plan_t;
+
+/*
+ * gemm_plan -- validate a problem and choose kernel and tile.  Host only: no
+ * device call, no allocation.
+ *   in_type : TG_BF16 or TG_FP16 (A and B alike)
+ *   out_type: TG_FP32, or the same type as in_type
+ *   m, n, k >= 0; leading dims as in the table above.
+ * Returns TG_OK, TG_ERR_INVALID (null plan, negative size, trans not 0/1,
+ * leading dim too small, size product overflow) or TG_ERR_UNSUPPORTED
+ * (dtype pair).  Tile choice follows the shape: M <= 32 with both operands
+ * K-contiguous selects the skinny kernel; otherwise the tile is sized so that
+ * the grid covers the chip, and the 16-byte vector loader is chosen when
+ * every leading dimension and every operand's contiguous extent is a
+ * multiple of 8 elements.
+ */
+tg_status gemm_plan(gemm_plan_t* plan, tg_dtype in_type, tg_dtype out_type, int trans_a, int trans_b,
+                    int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb, int64_t ldc);
+
+/*
+ * gemm_run -- enqueue C = op(A) op(B) on `stream` (0 = the null stream) and
+ * return without waiting.  A, B, C are device pointers.  If the plan chose the
+ * vector loader but a base pointer is not 16-byte aligned, the element-wise
+ * loader runs instead (same result).  M = 0 or N = 0 launches nothing; K = 0
+ * writes zeros to C.  Returns TG_ERR_INVALID for a null or stale plan
+ * (abi_version) or a null pointer with a nonzero extent, TG_ERR_UNSUPPORTED
+ * for a (variant, tile) pair that does not fit the problem, TG_ERR_HIP if the
+ * launch fails.
+ */
+tg_status gemm_run(const gemm_plan_t* plan, const void* A, const void* B, void* C, hipStream_t stream);
+
+/*
+ * bmm_run -- batched form: batch >= 0 independent products, operand b at
+ * A + b*stride_a, B + b*stride_b, C + b*stride_c (elements, >= 0; byte offsets
+ * are 64-bit).  batch = 0 launches nothing.  Same errors as gemm_run, plus
+ * TG_ERR_INVALID for a negative batch or stride.
+ */
+tg_status bmm_run(const gemm_plan_t* plan, int64_t batch, int64_t stride_a, int64_t stride_b,
+                  int64_t stride_c, const void* A, const void* B, void* C, hipStream_t stream);
+
+/* Static text for a status code ("ok", "invalid argument", ...). */
+const char* tg_status_str(tg_status s);
+
+/* TG_ABI_VERSION of the built library, to detect a header/library mismatch. */
+int32_t tg_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TGEMM_H */

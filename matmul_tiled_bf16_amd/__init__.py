@@ -1,0 +1,200 @@
+"""Tiled bf16/fp16 GEMM and batched GEMM for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libtgemm.so`` (``include/tgemm.h``): argument
+marshalling only -- every arithmetic step runs in the library's HIP kernels,
+and there is no fallback.  If the library is not built, every call raises.
+
+    import torch, matmul_tiled_bf16_amd as tg
+    C = tg.gemm(A, B, trans_b=True, out_dtype=torch.bfloat16)   # C = A @ B^T
+
+Matrices are row-major torch tensors whose last dimension is contiguous; a
+transpose is requested with ``trans_a``/``trans_b`` and is never materialised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtgemm.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "tgemm.h")
+
+TG_BF16, TG_FP16, TG_FP32 = 0, 1, 2
+TG_OK, TG_ERR_INVALID, TG_ERR_UNSUPPORTED, TG_ERR_HIP = 0, 1, 2, 3
+VARIANT_GENERIC, VARIANT_TILE, VARIANT_SKINNY = 0, 1, 2
+FLAG_EVEN_K, FLAG_VEC16 = 0x1, 0x2
+
+
+def _abi_version_from_header() -> int:
+    with open(HEADER) as f:
+        m = re.search(r"#define\s+TG_ABI_VERSION\s+(\d+)", f.read())
+    return int(m.group(1))
+
+
+class GemmPlan(ctypes.Structure):
+    """Mirror of gemm_plan_t."""
+    _fields_ = [
+        ("abi_version", ctypes.c_int32), ("in_type", ctypes.c_int32), ("out_type", ctypes.c_int32),
+        ("trans_a", ctypes.c_int32), ("trans_b", ctypes.c_int32),
+        ("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+        ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldc", ctypes.c_int64),
+        ("variant", ctypes.c_int32), ("tile", ctypes.c_int32),
+        ("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
+        ("wg_threads", ctypes.c_int32), ("stages", ctypes.c_int32), ("flags", ctypes.c_int32),
+        ("lds_bytes", ctypes.c_uint32), ("reserved0", ctypes.c_uint32),
+        ("workspace_bytes", ctypes.c_uint64),
+        ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64),
+    ]
+
+    def __repr__(self):
+        return ("GemmPlan(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_
+                                         if n != "reserved0") + ")")
+
+
+class TgError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m matmul_tiled_bf16_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        L.gemm_plan.restype = ctypes.c_int
+        L.gemm_plan.argtypes = [ctypes.POINTER(GemmPlan), ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                i64, i64, i64, i64, i64, i64]
+        L.gemm_run.restype = ctypes.c_int
+        L.gemm_run.argtypes = [ctypes.POINTER(GemmPlan), p, p, p, p]
+        L.bmm_run.restype = ctypes.c_int
+        L.bmm_run.argtypes = [ctypes.POINTER(GemmPlan), i64, i64, i64, i64, p, p, p, p]
+        L.tg_status_str.restype = ctypes.c_char_p
+        L.tg_status_str.argtypes = [ctypes.c_int]
+        L.tg_abi_version.restype = i32
+        L.tg_abi_version.argtypes = []
+        if L.tg_abi_version() != _abi_version_from_header():
+            raise RuntimeError("libtgemm.so was built from a different tgemm.h (ABI version mismatch)")
+        _lib = L
+    return _lib
+
+
+def status_str(s: int) -> str:
+    return lib().tg_status_str(int(s)).decode()
+
+
+def _dtype_code(dt) -> int:
+    import torch
+    if dt == torch.bfloat16:
+        return TG_BF16
+    if dt == torch.float16:
+        return TG_FP16
+    if dt == torch.float32:
+        return TG_FP32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def plan(m: int, n: int, k: int, *, trans_a: bool = False, trans_b: bool = False, in_dtype=None,
+         out_dtype=None, lda: Optional[int] = None, ldb: Optional[int] = None,
+         ldc: Optional[int] = None) -> GemmPlan:
+    """gemm_plan(): validate and choose kernel/tile (host only)."""
+    import torch
+    in_dtype = torch.bfloat16 if in_dtype is None else in_dtype
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    lda = lda if lda is not None else max(1, m if trans_a else k)
+    ldb = ldb if ldb is not None else max(1, k if trans_b else n)
+    ldc = ldc if ldc is not None else max(1, n)
+    p = GemmPlan()
+    st = lib().gemm_plan(ctypes.byref(p), _dtype_code(in_dtype), _dtype_code(out_dtype), int(trans_a),
+                         int(trans_b), m, n, k, lda, ldb, ldc)
+    if st != TG_OK:
+        raise TgError(st, "gemm_plan")
+    return p
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int:
+    return t.data_ptr() if hasattr(t, "data_ptr") else int(t)
+
+
+def gemm_run(p: GemmPlan, A, B, C, stream=None) -> None:
+    """gemm_run(): enqueue on ``stream`` (torch stream, raw handle, or current)."""
+    st = lib().gemm_run(ctypes.byref(p), _ptr(A), _ptr(B), _ptr(C), _stream_handle(stream))
+    if st != TG_OK:
+        raise TgError(st, "gemm_run")
+
+
+def bmm_run(p: GemmPlan, batch: int, stride_a: int, stride_b: int, stride_c: int, A, B, C,
+            stream=None) -> None:
+    st = lib().bmm_run(ctypes.byref(p), batch, stride_a, stride_b, stride_c, _ptr(A), _ptr(B), _ptr(C),
+                       _stream_handle(stream))
+    if st != TG_OK:
+        raise TgError(st, "bmm_run")
+
+
+def _check_matrix(X, name):
+    if not X.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if X.dim() not in (2, 3) or (X.shape[-1] > 1 and X.stride(-1) != 1):
+        raise ValueError(f"{name} must be a 2-D or 3-D tensor with a contiguous last dimension")
+
+
+def _ld(X) -> int:
+    return max(X.stride(-2), X.shape[-1], 1)
+
+
+def gemm(A, B, *, trans_a: bool = False, trans_b: bool = False, out_dtype=None, out=None, stream=None):
+    """C = op(A) @ op(B) for 2-D row-major tensors; returns C (new, or ``out``)."""
+    import torch
+    _check_matrix(A, "A")
+    _check_matrix(B, "B")
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must have the same dtype")
+    m, k = (A.shape[1], A.shape[0]) if trans_a else (A.shape[0], A.shape[1])
+    kb, n = (B.shape[1], B.shape[0]) if trans_b else (B.shape[0], B.shape[1])
+    if kb != k:
+        raise ValueError(f"inner dimensions differ: {k} vs {kb}")
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=A.device)
+    elif out.shape != (m, n) or out.dtype != out_dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    p = plan(m, n, k, trans_a=trans_a, trans_b=trans_b, in_dtype=A.dtype, out_dtype=out_dtype, lda=_ld(A),
+             ldb=_ld(B), ldc=_ld(out))
+    gemm_run(p, A, B, out, stream)
+    return out
+
+
+def bmm(A, B, *, trans_a: bool = False, trans_b: bool = False, out_dtype=None, out=None, stream=None):
+    """C[b] = op(A[b]) @ op(B[b]) for 3-D tensors [batch, rows, cols] (batch stride from the tensor)."""
+    import torch
+    _check_matrix(A, "A")
+    _check_matrix(B, "B")
+    if A.dim() != 3 or B.dim() != 3 or A.shape[0] != B.shape[0]:
+        raise ValueError("A and B must be 3-D with the same batch")
+    batch = A.shape[0]
+    m, k = (A.shape[2], A.shape[1]) if trans_a else (A.shape[1], A.shape[2])
+    kb, n = (B.shape[2], B.shape[1]) if trans_b else (B.shape[1], B.shape[2])
+    if kb != k:
+        raise ValueError(f"inner dimensions differ: {k} vs {kb}")
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((batch, m, n), dtype=out_dtype, device=A.device)
+    p = plan(m, n, k, trans_a=trans_a, trans_b=trans_b, in_dtype=A.dtype, out_dtype=out_dtype, lda=_ld(A),
+             ldb=_ld(B), ldc=_ld(out))
+    bmm_run(p, batch, A.stride(0), B.stride(0), out.stride(0), A, B, out, stream)
+    return out

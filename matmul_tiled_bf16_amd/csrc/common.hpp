@@ -1,0 +1,227 @@
+// common.hpp -- pieces shared by the gfx950 GEMM kernels: MFMA wrappers, LDS
+// layout (swizzle) and fragment reads, tile scheduling and the epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tg {
+
+#define TG_LDS __attribute__((address_space(3)))
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct GemmArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  void* C;
+  int64_t M, N, K;
+  int64_t lda, ldb, ldc;
+  int64_t sA, sB, sC;  // batch strides, elements
+  int64_t batch;
+  int32_t tiles_m, tiles_n;
+};
+
+using KernelFn = void (*)(GemmArgs);
+
+// ---------------------------------------------------------------- MFMA ---
+// v_mfma_f32_32x32x16: lane l supplies row (l & 31) of A and column (l & 31)
+// of B, each as 8 consecutive k starting at 8*(l >> 5); register r of the
+// result holds C[8*(r>>2) + 4*(l>>5) + (r&3)][l & 31].
+template <typename In>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
+template <>
+__device__ __forceinline__ f32x16 mfma32<__bf16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                  c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma32<_Float16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x32: lane l supplies row/column (l & 15) as 8 consecutive k
+// starting at 8*(l >> 4); register r holds C[4*(l>>4) + r][l & 15].
+template <typename In>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c);
+template <>
+__device__ __forceinline__ f32x4 mfma16<__bf16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                  0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma16<_Float16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// ------------------------------------------------------------ epilogue ---
+template <typename Out>
+__device__ __forceinline__ void store_out(void* C, int64_t off, float v);
+template <>
+__device__ __forceinline__ void store_out<float>(void* C, int64_t off, float v) {
+  static_cast<float*>(C)[off] = v;
+}
+template <>
+__device__ __forceinline__ void store_out<__bf16>(void* C, int64_t off, float v) {
+  static_cast<__bf16*>(C)[off] = (__bf16)v;  // v_cvt_pk_bf16_f32: nearest, ties to even
+}
+template <>
+__device__ __forceinline__ void store_out<_Float16>(void* C, int64_t off, float v) {
+  static_cast<_Float16*>(C)[off] = (_Float16)v;
+}
+
+// --------------------------------------------------------- LDS helpers ---
+__device__ __forceinline__ u32x4 lds_read16(const TG_LDS char* base, uint32_t off) {
+  return *(const TG_LDS u32x4*)(base + off);
+}
+__device__ __forceinline__ void lds_write16(TG_LDS char* base, uint32_t off, u32x4 v) {
+  *(TG_LDS u32x4*)(base + off) = v;
+}
+// Transposing read (ds_read_b64_tr_b16): in each group of 16 lanes, lane i
+// receives element (i & 3) of the 8-byte words addressed by lanes (i >> 2),
+// 4 + (i >> 2), 8 + (i >> 2) and 12 + (i >> 2).  So if lane s addresses row
+// r0 + (s >> 2), columns c0 + 4*(s & 3) .. +3 of a row-major 16-bit tile,
+// lane i ends up with column c0 + i of rows r0 .. r0+3.
+//
+// It is issued through inline assembly: the compiler's own form of this read
+// makes it wait for every outstanding HBM->LDS copy first (vmcnt(0)), which
+// would drain the K pipeline at every step.  The caller therefore owns the
+// LDS wait: call lds_wait_tr() on the results before using them.
+__device__ __forceinline__ u32x2 lds_read_tr(const TG_LDS char* base, uint32_t off) {
+  u32x2 v;
+  const uint32_t addr = (uint32_t)(size_t)(base + off);
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+// Wait for this wave's LDS reads, then mark the fragments as produced after
+// the wait so that no consumer is scheduled ahead of it.
+template <int N>
+__device__ __forceinline__ void lds_wait_tr(u32x4 (&frag)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(frag[i]));
+}
+
+// LDS swizzle, in 16-byte units.  A tile row is CH units long.
+//  * K-contiguous tiles (rows along M/N, CH = BK/8): fragment reads put 32
+//    lanes on 32 consecutive rows at one K offset; flipping the unit index by
+//    low row bits spreads each group of rows that shares a bank window.
+//  * M/N-contiguous tiles (rows along K): one transposing read has four rows
+//    at the same column offset per 16 lanes; flipping by a per-row pattern
+//    with distinct bits 1-2 and distinct bits 2-3 keeps those rows apart in
+//    both 128-byte and 256-byte bank windows.
+template <bool KCONTIG, int CH>
+__device__ __forceinline__ uint32_t swz_unit(uint32_t row) {
+  if constexpr (KCONTIG) {
+    if constexpr (CH >= 8)
+      return row & 7u;
+    else
+      return (row >> 1) & (uint32_t)(CH - 1);
+  } else {
+    const uint32_t r = row & 3u;
+    return ((r << 1) | ((r & 1u) << 3)) & (uint32_t)(CH - 1);
+  }
+}
+
+template <bool KCONTIG, int CH>
+__device__ __forceinline__ uint32_t swz_off(uint32_t row, uint32_t col) {
+  return row * (CH * 16u) + (((col >> 3) ^ swz_unit<KCONTIG, CH>(row)) << 4) + ((col & 7u) << 1);
+}
+
+// ------------------------------------------------------ tile scheduling ---
+// The hardware hands consecutive work-group ids to the 8 XCDs in turn.  Give
+// XCD x the contiguous id range [x*G/8, (x+1)*G/8) instead, then decode that
+// id in bands of GROUP_M tile rows so that work-groups running together on one
+// XCD share A rows and B columns in that XCD's L2.
+template <int GROUP_M>
+__device__ __forceinline__ void tile_coords(int32_t bid, int32_t tiles_m, int32_t tiles_n, int32_t& pm,
+                                            int32_t& pn) {
+  const int32_t G = tiles_m * tiles_n;
+  const int32_t per = G >> 3, rem = G & 7;
+  const int32_t x = bid & 7, local = bid >> 3;
+  const int32_t id = x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
+  const int32_t band = GROUP_M * tiles_n;
+  const int32_t bidx = id / band;
+  const int32_t first_m = bidx * GROUP_M;
+  const int32_t gsz = min(tiles_m - first_m, GROUP_M);
+  const int32_t in_band = id - bidx * band;
+  pm = first_m + in_band % gsz;
+  pn = in_band / gsz;
+}
+
+// ---------------------------------------------------- one LDS stage of MMA ---
+// A wave owns FM x FN blocks of 32x32 starting at (wm0, wn0) inside the tile.
+// K-contiguous operands are read with ds_read_b128 (8 consecutive k of one
+// row); M/N-contiguous ones with two transposing reads (4 k each), which
+// give the same k-to-register assignment.
+template <typename In, int FM, int FN, int BK, bool A_KC, bool B_KC, int A_CH, int B_CH>
+__device__ __forceinline__ void mma_stage(const TG_LDS char* sa, const TG_LDS char* sb, int wm0, int wn0, int lane,
+                                          f32x16 (&acc)[FM][FN]) {
+  const int li = lane & 31, lg = lane >> 5;
+  const int trh = lane >> 4, trs = lane & 15;
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) {
+    u32x4 af[FM], bf[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int rb = wm0 + i * 32;
+      if constexpr (A_KC) {
+        af[i] = lds_read16(sa, swz_off<true, A_CH>(rb + li, ks * 16 + lg * 8));
+      } else {
+        const int col = rb + 16 * (trh & 1) + 4 * (trs & 3);
+        const int kr = ks * 16 + 8 * (trh >> 1) + (trs >> 2);
+        const u32x2 lo = lds_read_tr(sa, swz_off<false, A_CH>(kr, col));
+        const u32x2 hi = lds_read_tr(sa, swz_off<false, A_CH>(kr + 4, col));
+        af[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int cb = wn0 + j * 32;
+      if constexpr (B_KC) {
+        bf[j] = lds_read16(sb, swz_off<true, B_CH>(cb + li, ks * 16 + lg * 8));
+      } else {
+        const int col = cb + 16 * (trh & 1) + 4 * (trs & 3);
+        const int kr = ks * 16 + 8 * (trh >> 1) + (trs >> 2);
+        const u32x2 lo = lds_read_tr(sb, swz_off<false, B_CH>(kr, col));
+        const u32x2 hi = lds_read_tr(sb, swz_off<false, B_CH>(kr + 4, col));
+        bf[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    }
+    if constexpr (!A_KC) lds_wait_tr(af);
+    if constexpr (!B_KC) lds_wait_tr(bf);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<In>(af[i], bf[j], acc[i][j]);
+  }
+}
+
+// Masked store of a wave's FM x FN 32x32 blocks (rows/cols past M/N dropped).
+template <typename Out, int FM, int FN>
+__device__ __forceinline__ void store_tile(void* Cb, int64_t ldc, int64_t M, int64_t N, int64_t r0, int64_t c0,
+                                           int lane, const f32x16 (&acc)[FM][FN]) {
+  const int li = lane & 31, lg = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t col = c0 + j * 32 + li;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = r0 + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+        if (row < M && col < N) store_out<Out>(Cb, row * ldc + col, acc[i][j][r]);
+      }
+    }
+  }
+}
+
+}  // namespace tg

@@ -1,0 +1,264 @@
+// tgemm.hip -- planner, kernel tables and the C ABI declared in include/tgemm.h.
+//
+// Planning follows the pages' block-parameter reasoning, restated for CDNA4
+// ("Optimize Triton Block Parameters", Steps 1-4 and Performance
+// requirements): classify the shape, keep the LDS budget
+// stages*(BM*BK + BK*BN)*2 bytes within the 160 KiB a gfx950 work-group may
+// hold, give small and ragged problems small tiles so the grid still covers
+// the 256 CUs, and take the 16-byte vector loader only where alignment allows
+// it ("Triton Optimization Reference", section 6).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tgemm.h"
+#include "common.hpp"
+#include "tiles.hpp"
+
+namespace tg {
+// Instance tables, one per (input, output, trans_a, trans_b); defined by the
+// objects built from inst_tile.hip and inst_skinny.hip.
+#define TG_DECLARE(in, out, ta, tb)                                  \
+  extern const KernelFn tile_##in##_##out##_##ta##tb[kNumTiles];     \
+  extern const KernelFn generic_##in##_##out##_##ta##tb[kNumGeneric];
+#define TG_DECLARE_IO(in, out) \
+  TG_DECLARE(in, out, 0, 0) TG_DECLARE(in, out, 0, 1) TG_DECLARE(in, out, 1, 0) TG_DECLARE(in, out, 1, 1)
+TG_DECLARE_IO(bf16, f32)
+TG_DECLARE_IO(bf16, bf16)
+TG_DECLARE_IO(f16, f32)
+TG_DECLARE_IO(f16, f16)
+extern const KernelFn skinny_table[2][2][kNumSkinny];
+}  // namespace tg
+
+namespace {
+
+using tg::KernelFn;
+using tg::kGenericTiles;
+using tg::kNumGeneric;
+using tg::kNumSkinny;
+using tg::kNumTiles;
+using tg::kSkinny;
+using tg::kTiles;
+using tg::TileShape;
+
+#define TG_ROW(in, out) \
+  {tg::tile_##in##_##out##_00, tg::tile_##in##_##out##_01, tg::tile_##in##_##out##_10, tg::tile_##in##_##out##_11}
+#define TG_GROW(in, out)                                                                              \
+  {tg::generic_##in##_##out##_00, tg::generic_##in##_##out##_01, tg::generic_##in##_##out##_10, \
+   tg::generic_##in##_##out##_11}
+
+// [in bf16/fp16][out fp32/same][2*trans_a + trans_b]
+const KernelFn* const kTileTables[2][2][4] = {{TG_ROW(bf16, f32), TG_ROW(bf16, bf16)},
+                                              {TG_ROW(f16, f32), TG_ROW(f16, f16)}};
+const KernelFn* const kGenericTables[2][2][4] = {{TG_GROW(bf16, f32), TG_GROW(bf16, bf16)},
+                                                 {TG_GROW(f16, f32), TG_GROW(f16, f16)}};
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The vector kernel reads 16-byte units along each operand's contiguous
+// dimension: every leading dimension and contiguous extent must be a multiple
+// of 8 elements, and one tile's span of rows must stay addressable by the
+// 31-bit buffer offsets.
+bool vec_ok(const gemm_plan_t& p) {
+  const int64_t a_contig = p.trans_a ? p.m : p.k;
+  const int64_t b_contig = p.trans_b ? p.k : p.n;
+  const int64_t span = (int64_t)1 << 30;  // 256 rows * ld * 2 bytes < 2^31
+  return p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % 8 == 0 && a_contig % 8 == 0 && b_contig % 8 == 0 &&
+         a_contig >= 8 && b_contig >= 8 && p.lda * 256 < span && p.ldb * 256 < span;
+}
+
+bool skinny_ok(const gemm_plan_t& p) {
+  return !p.trans_a && p.trans_b && p.m >= 1 && p.m <= 32 && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.k % 8 == 0 &&
+         p.k >= 8;
+}
+
+bool skinny_fits(int t, int64_t m) { return m <= 16 * kSkinny[t].mb; }
+
+int skinny_choose(int64_t m, int64_t n) {
+  if (m > 16) return 1;
+  return (n / 32 >= 256) ? 0 : 2;
+}
+
+// Tile choice by shape class.  Large problems take the biggest tile the grid
+// can still fill the chip with; small and ragged ones take smaller tiles so
+// that there are at least ~256 work-groups ("Optimize Triton Block
+// Parameters": shape-specific tuning, a small M wants a small BLOCK_M).
+int choose_tile(int64_t m, int64_t n) {
+  auto tiles = [&](int t) { return cdiv(m, kTiles[t].bm) * cdiv(n, kTiles[t].bn); };
+  if (m <= 32) return 5;
+  if (tiles(2) >= 512) return 2;  // 256x256: >= 2 work-groups per CU
+  if (tiles(1) >= 256) return 1;  // 128x128
+  return 0;                       // 64x64
+}
+
+int choose_generic(int64_t m, int64_t n) { return cdiv(m, 128) * cdiv(n, 128) >= 256 ? 1 : 0; }
+
+struct Launch {
+  int bm, bn, bk, threads, stages, lds;
+};
+
+Launch launch_shape(int variant, int tile) {
+  if (variant == TG_VARIANT_SKINNY) {
+    const tg::SkinnyShape& s = kSkinny[tile];
+    return Launch{16 * s.mb, 16 * s.nblk, 32 * s.unroll, 64 * s.waves, 1, tg::skinny_lds_of(s)};
+  }
+  const TileShape& t = variant == TG_VARIANT_TILE ? kTiles[tile] : kGenericTiles[tile];
+  return Launch{t.bm, t.bn, t.bk, 64 * t.wm * t.wn, t.stages, tg::lds_bytes_of(t)};
+}
+
+void fill_shape(gemm_plan_t* p) {
+  const Launch l = launch_shape(p->variant, p->tile);
+  p->bm = l.bm;
+  p->bn = l.bn;
+  p->bk = l.bk;
+  p->wg_threads = l.threads;
+  p->stages = l.stages;
+  p->lds_bytes = (uint32_t)l.lds;
+  p->tiles_m = p->variant == TG_VARIANT_SKINNY ? 1 : cdiv(p->m, p->bm);
+  p->tiles_n = cdiv(p->n, p->bn);
+  p->flags = (p->flags & ~TG_FLAG_EVEN_K) | ((p->bk > 0 && p->k % p->bk == 0) ? TG_FLAG_EVEN_K : 0);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tg_status_str(tg_status s) {
+  switch (s) {
+    case TG_OK: return "ok";
+    case TG_ERR_INVALID: return "invalid argument";
+    case TG_ERR_UNSUPPORTED: return "unsupported";
+    case TG_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int32_t tg_abi_version(void) { return TG_ABI_VERSION; }
+
+tg_status gemm_plan(gemm_plan_t* plan, tg_dtype in_type, tg_dtype out_type, int trans_a, int trans_b, int64_t m,
+                    int64_t n, int64_t k, int64_t lda, int64_t ldb, int64_t ldc) {
+  if (!plan) return TG_ERR_INVALID;
+  gemm_plan_t p = {};
+  p.abi_version = -1;
+  *plan = p;
+  if (m < 0 || n < 0 || k < 0) return TG_ERR_INVALID;
+  if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return TG_ERR_INVALID;
+  const int64_t lim = (int64_t)1 << 31;
+  if (m >= lim || n >= lim || k >= lim) return TG_ERR_INVALID;
+  const int64_t min_lda = trans_a ? m : k, min_ldb = trans_b ? k : n;
+  if (lda < (min_lda > 1 ? min_lda : 1) || ldb < (min_ldb > 1 ? min_ldb : 1) || ldc < (n > 1 ? n : 1))
+    return TG_ERR_INVALID;
+  // element offsets of every operand must stay far inside int64
+  const int64_t big = (int64_t)1 << 60;
+  if (lda > big / ((trans_a ? k : m) + 1) || ldb > big / ((trans_b ? n : k) + 1) || ldc > big / (m + 1))
+    return TG_ERR_INVALID;
+  if (in_type != TG_BF16 && in_type != TG_FP16) return TG_ERR_UNSUPPORTED;
+  if (out_type != TG_FP32 && out_type != in_type) return TG_ERR_UNSUPPORTED;
+
+  p.in_type = in_type;
+  p.out_type = out_type;
+  p.trans_a = trans_a;
+  p.trans_b = trans_b;
+  p.m = m;
+  p.n = n;
+  p.k = k;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = ldc;
+  p.workspace_bytes = 0;
+  p.flags = vec_ok(p) ? TG_FLAG_VEC16 : 0;
+  if (skinny_ok(p)) {
+    p.variant = TG_VARIANT_SKINNY;
+    p.tile = skinny_choose(m, n);
+  } else if (p.flags & TG_FLAG_VEC16) {
+    p.variant = TG_VARIANT_TILE;
+    p.tile = choose_tile(m, n);
+  } else {
+    p.variant = TG_VARIANT_GENERIC;
+    p.tile = choose_generic(m, n);
+  }
+  fill_shape(&p);
+  if (p.tiles_m * p.tiles_n >= lim) return TG_ERR_INVALID;
+  p.abi_version = TG_ABI_VERSION;
+  *plan = p;
+  return TG_OK;
+}
+
+static tg_status launch(const gemm_plan_t* plan, int64_t batch, int64_t sA, int64_t sB, int64_t sC, const void* A,
+                        const void* B, void* C, hipStream_t stream) {
+  if (!plan || plan->abi_version != TG_ABI_VERSION) return TG_ERR_INVALID;
+  if (batch < 0 || sA < 0 || sB < 0 || sC < 0) return TG_ERR_INVALID;
+  const gemm_plan_t& p = *plan;
+  if (p.m == 0 || p.n == 0 || batch == 0) return TG_OK;
+  if (!C) return TG_ERR_INVALID;
+  if (p.k > 0 && (!A || !B)) return TG_ERR_INVALID;
+  if (p.in_type < 0 || p.in_type > 1 || (p.out_type != TG_FP32 && p.out_type != p.in_type)) return TG_ERR_INVALID;
+  if (batch > 1 && sC < (p.m - 1) * p.ldc + p.n) return TG_ERR_INVALID;  // batches' outputs would overlap
+
+  // re-validate the (variant, tile) pair: callers may override it
+  int variant = p.variant, tile = p.tile;
+  if (variant == TG_VARIANT_SKINNY) {
+    if (tile < 0 || tile >= kNumSkinny || !skinny_ok(p) || !skinny_fits(tile, p.m)) return TG_ERR_UNSUPPORTED;
+  } else if (variant == TG_VARIANT_TILE) {
+    if (tile < 0 || tile >= kNumTiles || !vec_ok(p)) return TG_ERR_UNSUPPORTED;
+  } else if (variant == TG_VARIANT_GENERIC) {
+    if (tile < 0 || tile >= kNumGeneric) return TG_ERR_UNSUPPORTED;
+  } else {
+    return TG_ERR_UNSUPPORTED;
+  }
+  // vector paths need 16-byte aligned bases and batch strides; else gather element-wise
+  const bool aligned = ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && ((uintptr_t)C % 16 == 0) &&
+                       (batch == 1 || (sA % 8 == 0 && sB % 8 == 0 && sC % 8 == 0));
+  if (variant != TG_VARIANT_GENERIC && !aligned) {
+    variant = TG_VARIANT_GENERIC;
+    tile = choose_generic(p.m, p.n);
+  }
+
+  tg::GemmArgs a;
+  a.A = static_cast<const uint16_t*>(A);
+  a.B = static_cast<const uint16_t*>(B);
+  a.C = C;
+  a.M = p.m;
+  a.N = p.n;
+  a.K = p.k;
+  a.lda = p.lda;
+  a.ldb = p.ldb;
+  a.ldc = p.ldc;
+  a.sA = sA;
+  a.sB = sB;
+  a.sC = sC;
+  a.batch = batch;
+
+  const Launch l = launch_shape(variant, tile);
+  const int io = p.in_type == TG_BF16 ? 0 : 1, oo = p.out_type == TG_FP32 ? 0 : 1;
+  KernelFn fn;
+  if (variant == TG_VARIANT_SKINNY) {
+    a.tiles_m = 1;
+    a.tiles_n = (int32_t)cdiv(p.n, l.bn);
+    fn = tg::skinny_table[io][oo][tile];
+  } else {
+    a.tiles_m = (int32_t)cdiv(p.m, l.bm);
+    a.tiles_n = (int32_t)cdiv(p.n, l.bn);
+    const int tr = 2 * p.trans_a + p.trans_b;
+    fn = variant == TG_VARIANT_TILE ? kTileTables[io][oo][tr][tile] : kGenericTables[io][oo][tr][tile];
+  }
+  const int64_t groups = (int64_t)a.tiles_m * a.tiles_n;
+  if (groups >= ((int64_t)1 << 31)) return TG_ERR_INVALID;
+  const dim3 grid((unsigned)groups, (unsigned)(batch < 65535 ? batch : 65535));
+  if (l.lds > 64 * 1024) {
+    if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, l.lds) != hipSuccess)
+      return TG_ERR_HIP;
+  }
+  hipLaunchKernelGGL(fn, grid, dim3(l.threads), (size_t)l.lds, stream, a);
+  return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
+}
+
+tg_status gemm_run(const gemm_plan_t* plan, const void* A, const void* B, void* C, hipStream_t stream) {
+  return launch(plan, 1, 0, 0, 0, A, B, C, stream);
+}
+
+tg_status bmm_run(const gemm_plan_t* plan, int64_t batch, int64_t stride_a, int64_t stride_b, int64_t stride_c,
+                  const void* A, const void* B, void* C, hipStream_t stream) {
+  return launch(plan, batch, stride_a, stride_b, stride_c, A, B, C, stream);
+}
+
+}  // extern "C"

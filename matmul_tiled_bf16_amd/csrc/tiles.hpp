@@ -1,0 +1,50 @@
+// tiles.hpp -- tile tables shared by the planner and the kernel instances.
+//
+// Each entry fixes the work-group tile (BM x BN), the K step (BK), the wave
+// grid (WM x WN, 64 lanes per wave) and the LDS ring depth.  The LDS budget
+// stages * (BM*BK + BK*BN) * 2 bytes stays within the 160 KiB one gfx950
+// work-group may hold ("Optimize Triton Block Parameters", Step 2: stages
+// times the A/B tile pair, checked against on-chip capacity).
+#pragma once
+
+namespace tg {
+
+struct TileShape {
+  int bm, bn, bk, wm, wn, stages;
+};
+
+constexpr TileShape kTiles[] = {
+    {64, 64, 64, 2, 2, 2},     // 0: 32x32 per wave -- small and ragged problems
+    {128, 128, 64, 2, 2, 2},   // 1: 64x64 per wave
+    {256, 256, 32, 2, 2, 4},   // 2: 128x128 per wave, 4-deep ring -- large, compute-bound
+    {256, 128, 64, 2, 2, 2},   // 3: 128x64 per wave
+    {128, 256, 64, 2, 2, 2},   // 4: 64x128 per wave
+    {32, 128, 64, 1, 4, 2},    // 5: one 32-row tile -- thin M
+    {128, 128, 32, 2, 2, 4},   // 6: 64x64 per wave, 4-deep ring
+    {256, 256, 64, 2, 2, 2},   // 7: 128x128 per wave, 2-deep ring
+};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
+constexpr TileShape kGenericTiles[] = {
+    {64, 64, 64, 2, 2, 2},
+    {128, 128, 64, 2, 2, 2},
+};
+constexpr int kNumGeneric = sizeof(kGenericTiles) / sizeof(kGenericTiles[0]);
+
+constexpr int lds_bytes_of(const TileShape& t) { return t.stages * (t.bm * t.bk + t.bk * t.bn) * 2; }
+
+// Skinny (M <= 32) streaming kernel: MB 16-row blocks, NBLK 16-column blocks
+// per work-group, WAVES waves splitting K, UNROLL 32-deep K blocks in flight.
+struct SkinnyShape {
+  int mb, nblk, waves, unroll;
+};
+constexpr SkinnyShape kSkinny[] = {
+    {1, 2, 8, 4},  // 0: M <= 16, 32 columns per work-group
+    {2, 2, 8, 4},  // 1: M <= 32
+    {1, 1, 8, 8},  // 2: M <= 16, 16 columns per work-group
+    {1, 4, 8, 2},  // 3: M <= 16, 64 columns per work-group
+};
+constexpr int kNumSkinny = sizeof(kSkinny) / sizeof(kSkinny[0]);
+constexpr int skinny_lds_of(const SkinnyShape& s) { return s.waves * s.mb * s.nblk * 64 * 16; }
+
+}  // namespace tg

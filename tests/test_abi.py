@@ -1,0 +1,195 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+its plan struct matches the header, and gemm_plan()/the run-time argument
+checks behave as include/tgemm.h documents.  No kernel is launched here."""
+import ctypes
+import json
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import matmul_tiled_bf16_amd as tg
+from matmul_tiled_bf16_amd import roofline
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tgemm.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\([^;{]*\)\s*;", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"gemm_plan", "gemm_run", "bmm_run", "tg_status_str", "tg_abi_version"} <= set(names)
+    L = tg.lib()
+    for n in names:
+        assert hasattr(L, n), f"libtgemm.so does not export {n}"
+    nm = subprocess.run(["nm", "-D", "--defined-only", tg.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", nm, flags=re.M), f"{n} not a defined text symbol"
+
+
+def test_abi_version_matches_header():
+    assert tg.lib().tg_abi_version() == tg._abi_version_from_header()
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_plan_struct_layout_matches_header(tmp_path):
+    fields = [f for f, _ in tg.GemmPlan._fields_]
+    prog = ['#include <stdio.h>', '#include <stddef.h>', '#include "tgemm.h"', 'int main(void) {',
+            'printf("%zu\\n", sizeof(gemm_plan_t));']
+    prog += [f'printf("%zu\\n", offsetof(gemm_plan_t, {f}));' for f in fields]
+    prog += ['return 0; }']
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(prog))
+    exe = tmp_path / "layout"
+    r = subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", f"-I{os.path.dirname(HEADER)}", "-I/opt/rocm/include",
+                        str(c), "-o", str(exe)], capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("the HIP runtime header does not compile with plain gcc here: " + r.stderr[-300:])
+    out = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(tg.GemmPlan)
+    for f, off in zip(fields, out[1:]):
+        assert getattr(tg.GemmPlan, f).offset == off, f
+
+
+def test_status_strings():
+    assert tg.status_str(tg.TG_OK) == "ok"
+    assert tg.status_str(tg.TG_ERR_INVALID) == "invalid argument"
+    assert tg.status_str(tg.TG_ERR_UNSUPPORTED) == "unsupported"
+    assert tg.status_str(tg.TG_ERR_HIP) == "HIP launch error"
+    assert tg.status_str(99) == "unknown status"
+
+
+def raw_plan(in_t=0, out_t=2, ta=0, tb=0, m=64, n=64, k=64, lda=None, ldb=None, ldc=None):
+    p = tg.GemmPlan()
+    lda = lda if lda is not None else max(1, m if ta else k)
+    ldb = ldb if ldb is not None else max(1, k if tb else n)
+    ldc = ldc if ldc is not None else max(1, n)
+    st = tg.lib().gemm_plan(ctypes.byref(p), in_t, out_t, ta, tb, m, n, k, lda, ldb, ldc)
+    return st, p
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(m=-1), tg.TG_ERR_INVALID),
+    (dict(k=-5), tg.TG_ERR_INVALID),
+    (dict(ta=2), tg.TG_ERR_INVALID),
+    (dict(tb=-1), tg.TG_ERR_INVALID),
+    (dict(m=64, k=100, lda=99), tg.TG_ERR_INVALID),          # lda < K
+    (dict(ta=1, m=100, k=64, lda=99), tg.TG_ERR_INVALID),    # transposed A: lda < M
+    (dict(n=100, ldb=99), tg.TG_ERR_INVALID),
+    (dict(tb=1, k=100, ldb=99), tg.TG_ERR_INVALID),
+    (dict(n=100, ldc=99), tg.TG_ERR_INVALID),
+    (dict(m=1 << 31), tg.TG_ERR_INVALID),
+    (dict(in_t=2), tg.TG_ERR_UNSUPPORTED),                    # fp32 inputs
+    (dict(in_t=1, out_t=0), tg.TG_ERR_UNSUPPORTED),           # fp16 -> bf16
+    (dict(in_t=0, out_t=1), tg.TG_ERR_UNSUPPORTED),           # bf16 -> fp16
+    (dict(in_t=0, out_t=0), tg.TG_OK),
+    (dict(in_t=1, out_t=1), tg.TG_OK),
+    (dict(in_t=1, out_t=2), tg.TG_OK),
+    (dict(m=0, n=0, k=0), tg.TG_OK),
+])
+def test_plan_validation(kw, status):
+    st, p = raw_plan(**kw)
+    assert st == status
+    if st != tg.TG_OK:
+        assert p.abi_version != tg._abi_version_from_header(), "failed plan must not look valid"
+
+
+def test_null_plan_pointer():
+    assert tg.lib().gemm_plan(None, 0, 2, 0, 0, 1, 1, 1, 1, 1, 1) == tg.TG_ERR_INVALID
+    assert tg.lib().gemm_run(None, None, None, None, None) == tg.TG_ERR_INVALID
+    assert tg.lib().bmm_run(None, 1, 0, 0, 0, None, None, None, None) == tg.TG_ERR_INVALID
+
+
+def test_plan_choices_for_the_workloads():
+    # 256^3 NN fp32 out: too few 128-tiles to fill 256 CUs -> 64x64 tiles, K multiple of 64
+    p = tg.plan(256, 256, 256)
+    assert (p.variant, p.bm, p.bn, p.flags & tg.FLAG_EVEN_K, p.flags & tg.FLAG_VEC16) == (
+        tg.VARIANT_TILE, 64, 64, tg.FLAG_EVEN_K, tg.FLAG_VEC16)
+    # 1000^3, every transpose: vector path (1000 = 8*125), ragged K tail
+    for ta in (0, 1):
+        for tb in (0, 1):
+            p = tg.plan(1000, 1000, 1000, trans_a=ta, trans_b=tb)
+            assert p.variant == tg.VARIANT_TILE and p.flags & tg.FLAG_VEC16 and not p.flags & tg.FLAG_EVEN_K
+            assert p.tiles_m * p.tiles_n >= 64
+    # skinny M = 16, B stored N x K
+    import torch
+    p = tg.plan(16, 8192, 8192, trans_b=True, out_dtype=torch.bfloat16)
+    assert p.variant == tg.VARIANT_SKINNY and p.bm >= 16
+    # attention-shaped batched products and the big square GEMM
+    p = tg.plan(2048, 2048, 128, trans_b=True)
+    assert p.variant == tg.VARIANT_TILE and p.flags & tg.FLAG_EVEN_K
+    p = tg.plan(2048, 128, 2048)
+    assert p.variant == tg.VARIANT_TILE
+    p = tg.plan(8192, 8192, 8192, out_dtype=torch.bfloat16)
+    assert (p.variant, p.bm, p.bn) == (tg.VARIANT_TILE, 256, 256) and p.tiles_m * p.tiles_n == 1024
+    assert p.workspace_bytes == 0
+
+
+def test_odd_shapes_take_the_generic_loader():
+    st, p = raw_plan(m=17, n=33, k=63)          # K not a multiple of 8
+    assert st == tg.TG_OK and p.variant == tg.VARIANT_GENERIC and not p.flags & tg.FLAG_VEC16
+    st, p = raw_plan(m=64, n=64, k=64, lda=65)  # odd leading dimension
+    assert st == tg.TG_OK and p.variant == tg.VARIANT_GENERIC
+
+
+def test_lds_budget_matches_the_staging_formula_and_fits():
+    for m, n, k in [(256, 256, 256), (1000, 1000, 1000), (8192, 8192, 8192), (2048, 128, 2048), (17, 33, 63)]:
+        st, p = raw_plan(m=m, n=n, k=k)
+        assert st == tg.TG_OK
+        if p.variant != tg.VARIANT_SKINNY:
+            assert p.lds_bytes == roofline.lds_budget(p.bm, p.bn, p.bk, p.stages)
+        assert p.lds_bytes <= roofline.MI355X_LDS_PER_WORKGROUP
+
+
+def test_run_time_checks_that_need_no_gpu():
+    st, p = raw_plan(m=64, n=64, k=64)
+    assert st == tg.TG_OK
+    L = tg.lib()
+    # a stale or foreign plan
+    q = tg.GemmPlan.from_buffer_copy(p)
+    q.abi_version = 12345
+    assert L.gemm_run(ctypes.byref(q), 16, 16, 16, None) == tg.TG_ERR_INVALID
+    # null output / inputs with nonzero extents
+    assert L.gemm_run(ctypes.byref(p), 16, 16, None, None) == tg.TG_ERR_INVALID
+    assert L.gemm_run(ctypes.byref(p), None, 16, 16, None) == tg.TG_ERR_INVALID
+    # bad batch arguments; overlapping outputs across the batch
+    assert L.bmm_run(ctypes.byref(p), -1, 0, 0, 0, 16, 16, 16, None) == tg.TG_ERR_INVALID
+    assert L.bmm_run(ctypes.byref(p), 2, -1, 0, 4096, 16, 16, 16, None) == tg.TG_ERR_INVALID
+    assert L.bmm_run(ctypes.byref(p), 2, 0, 0, 64, 16, 16, 16, None) == tg.TG_ERR_INVALID
+    # overridden (variant, tile) pairs that do not exist or do not fit
+    for variant, tile in [(7, 0), (tg.VARIANT_TILE, 99), (tg.VARIANT_GENERIC, -1), (tg.VARIANT_SKINNY, 0)]:
+        q = tg.GemmPlan.from_buffer_copy(p)
+        q.variant, q.tile = variant, tile
+        assert L.gemm_run(ctypes.byref(q), 16, 16, 16, None) == tg.TG_ERR_UNSUPPORTED
+    st, r = raw_plan(m=17, n=33, k=63)
+    r.variant = tg.VARIANT_TILE                 # vector loader on a shape it cannot serve
+    assert L.gemm_run(ctypes.byref(r), 16, 16, 16, None) == tg.TG_ERR_UNSUPPORTED
+    # empty problems launch nothing and succeed
+    st, e = raw_plan(m=0, n=64, k=64)
+    assert L.gemm_run(ctypes.byref(e), None, None, None, None) == tg.TG_OK
+    st, e = raw_plan(m=64, n=64, k=64)
+    assert L.bmm_run(ctypes.byref(e), 0, 0, 0, 0, None, None, None, None) == tg.TG_OK
+
+
+def test_page_figures_pin_the_roofline_arithmetic():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "page_figures.json")))
+    r = g["ridge_a100_fp16"]
+    assert roofline.ridge(r["peak_flops"], r["peak_bytes"]) == r["ridge"]
+    f = g["gemm_fp16_bytes_formula"]
+    assert roofline.gemm_flops(f["m"], f["n"], f["k"]) == f["flops"]
+    assert roofline.gemm_bytes(f["m"], f["n"], f["k"], in_size=2, out_size=2) == f["bytes"]
+    s = g["smem_overflow_example"]
+    assert roofline.lds_budget(s["bm"], s["bn"], s["bk"], s["stages"], s["elem"]) == s["bytes"] > s["a100_limit_bytes"]
+    a = g["accumulator_example"]
+    assert roofline.accumulator_bytes(a["bm"], a["bn"]) == a["bytes"]
+    # the same arithmetic on MI355X: the 8192^3 GEMM is MFMA-bound, the M=16 one HBM-bound
+    assert roofline.bound(8192, 8192, 8192, out_size=2) == "mfma"
+    assert roofline.bound(16, 8192, 8192, out_size=2) == "hbm"
