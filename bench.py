@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Benchmark of the tiled GEMM/BMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = plan + launch of the whole product for one set of synthetic inputs
+already resident in HBM (gemm_plan on the host, then gemm_run / bmm_run).
+W untimed steps, then exactly K timed steps between two device
+synchronisations.  Prints one JSON line.
+
+Workloads (seeded synthetic inputs from synth/):
+  square_8192   8192^3, NN, bf16 in, bf16 out        (default; MFMA-bound)
+  skinny_16     M=16, N=K=8192, B stored N x K, bf16 out  (HBM-bound)
+  attention_s   128 x (2048x2048x128) S = Q K^T, fp32 out (HBM-bound)
+  attention_o   128 x (2048x128x2048) O = P V,   fp32 out (HBM-bound)
+  ragged_1000   1000^3 NN, fp32 out
+  square_256    256^3 NN, fp32 out
+
+The "roofline" object rates the dominant kernel against MI355X's published
+peak (dense bf16 MFMA 2.5 PFLOP/s, HBM3E 8 TB/s); its duration is the mean of
+per-launch HIP events on the launch stream.  "cpu_baseline" times the CPU
+oracle on a bounded sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "bf16 GEMM/BMM TFLOP/s and % of MFMA peak (GB/s and % HBM for skinny M)"
+PEAK_MFMA = 2.5e15
+PEAK_HBM = 8.0e12
+
+
+def problems(name):
+    import synth
+    if name == "square_8192":
+        return synth.square_8192()
+    if name == "skinny_16":
+        return synth.skinny_16()
+    if name == "attention_s":
+        return synth.attention_bmm()[:1]
+    if name == "attention_o":
+        return synth.attention_bmm()[1:]
+    if name == "ragged_1000":
+        return synth.ragged_1000()[:1]
+    if name == "square_256":
+        return synth.square_256()
+    raise SystemExit(f"unknown workload {name}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="square_8192")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="copies of B to cycle through (defeats the 256 MiB Infinity Cache); "
+                         "default 4 for HBM-bound workloads, 1 otherwise")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the design notes describe how the product would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import matmul_tiled_bf16_amd as tg
+    from matmul_tiled_bf16_amd import roofline
+
+    (p,) = problems(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tin = torch.bfloat16 if p.in_dtype == "bf16" else torch.float16
+    tout = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[p.out_dtype]
+    out_size = {"fp32": 4, "bf16": 2, "fp16": 2}[p.out_dtype]
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(tin).to(dev)
+
+    flops = roofline.gemm_flops(p.m, p.n, p.k, p.batch)
+    nbytes = roofline.gemm_bytes(p.m, p.n, p.k, 2, out_size, p.batch)
+    bound = roofline.bound(p.m, p.n, p.k, 2, out_size, p.batch, PEAK_MFMA, PEAK_HBM)
+    rotate = args.rotate or (4 if bound == "hbm" else 1)
+
+    A = up(p.A)
+    Bs = [up(p.B)] + [up(p.B).clone() for _ in range(rotate - 1)]
+    Cs = [torch.empty((p.batch, p.m, p.n) if p.batch > 1 else (p.m, p.n), dtype=tout, device=dev)
+          for _ in range(min(rotate, 2))]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        pl = tg.plan(p.m, p.n, p.k, trans_a=p.trans_a, trans_b=p.trans_b, in_dtype=tin, out_dtype=tout,
+                     lda=p.lda, ldb=p.ldb, ldc=p.ldc)
+        B = Bs[i % len(Bs)]
+        C = Cs[i % len(Cs)]
+        if p.batch == 1:
+            tg.gemm_run(pl, A, B, C, stream)
+        else:
+            tg.bmm_run(pl, p.batch, p.stride_a, p.stride_b, p.stride_c, A, B, C, stream)
+        return pl
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        pl = step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kernel_s = float(np.mean(kms)) / 1e3
+    ms_per_step = wall * 1e3 / args.steps
+    assert torch.isfinite(Cs[0].float()).all().item(), "non-finite output"
+
+    tflops = flops / (ms_per_step / 1e3) / 1e12
+    gbps = nbytes / (ms_per_step / 1e3) / 1e9
+    if bound == "mfma":
+        value, unit = tflops, "TFLOP/s"
+        achieved, peak, runit = flops / kernel_s / 1e12, PEAK_MFMA / 1e12, "TFLOP/s"
+    else:
+        value, unit = gbps, "GB/s"
+        achieved, peak, runit = nbytes / kernel_s / 1e9, PEAK_HBM / 1e9, "GB/s"
+
+    trans = ("T" if p.trans_a else "N") + ("T" if p.trans_b else "N")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if p.in_dtype == "bf16" else "fp16",
+        "data": "synthetic",
+        "config": {"workload": p.name, "m": p.m, "n": p.n, "k": p.k, "batch": p.batch, "op": trans,
+                   "in_dtype": p.in_dtype, "out_dtype": p.out_dtype, "b_copies": len(Bs),
+                   "variant": int(pl.variant), "tile": [int(pl.bm), int(pl.bn), int(pl.bk)]},
+        "tflops": round(tflops, 2),
+        "pct_mfma_peak": round(100 * flops / (ms_per_step / 1e3) / PEAK_MFMA, 2),
+        "gbps": round(gbps, 1),
+        "pct_hbm_peak": round(100 * nbytes / (ms_per_step / 1e3) / PEAK_HBM, 2),
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": runit,
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel_ms": round(kernel_s * 1e3, 5),
+                     "algorithmic": {"flops": flops, "bytes": nbytes}},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(p, unit, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(p, unit, seconds):
+    """Time the CPU oracle on a seeded sample of output elements (~`seconds` of work)."""
+    import oracle
+    import synth
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    calib = synth.sample_indices(77, p.batch, p.m, p.n, count=256, edges=())
+    t0 = time.perf_counter()
+    oracle.gemm_problem(p, idx=calib)
+    dt = max(time.perf_counter() - t0, 1e-4)
+    count = int(max(256, min(50_000_000, 256 * seconds / dt)))
+    idx = synth.sample_indices(78, p.batch, p.m, p.n, count=count, edges=())
+    t0 = time.perf_counter()
+    oracle.gemm_problem(p, idx=idx)
+    t = time.perf_counter() - t0
+    flops = 2.0 * p.k * len(idx)
+    # the same work rate expressed in the workload's unit
+    if unit == "TFLOP/s":
+        v = flops / t / 1e12
+    else:
+        total_flops = 2.0 * p.m * p.n * p.k * p.batch
+        total_bytes = p.batch * ((p.m * p.k + p.k * p.n) * 2 + p.m * p.n * (4 if p.out_dtype == "fp32" else 2))
+        v = (flops / t) / total_flops * total_bytes / 1e9
+    return {"value": round(v, 6), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{len(idx)} seeded output elements of the same workload (each a {p.k}-term fp64 dot "
+                      f"product), {t:.1f} s on {threads} threads; full problem would take "
+                      f"{t * p.m * p.n * p.batch / len(idx):.0f} s"}
+
+
+if __name__ == "__main__":
+    main()
