@@ -66,6 +66,7 @@ def main():
                     help="copies of B to cycle through (defeats the 256 MiB Infinity Cache); "
                          "default 4 for HBM-bound workloads, 1 otherwise")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tile", type=int, default=None, help="override the planner's tile (same variant)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
 
@@ -103,6 +104,8 @@ def main():
     def step(i):
         pl = tg.plan(p.m, p.n, p.k, trans_a=p.trans_a, trans_b=p.trans_b, in_dtype=tin, out_dtype=tout,
                      lda=p.lda, ldb=p.ldb, ldc=p.ldc)
+        if args.tile is not None:
+            pl.tile = args.tile
         B = Bs[i % len(Bs)]
         C = Cs[i % len(Cs)]
         if p.batch == 1:

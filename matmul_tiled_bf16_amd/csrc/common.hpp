@@ -31,9 +31,13 @@ struct GemmArgs {
 using KernelFn = void (*)(GemmArgs);
 
 // ---------------------------------------------------------------- MFMA ---
-// v_mfma_f32_32x32x16: lane l supplies row (l & 31) of A and column (l & 31)
-// of B, each as 8 consecutive k starting at 8*(l >> 5); register r of the
-// result holds C[8*(r>>2) + 4*(l>>5) + (r&3)][l & 31].
+// v_mfma_f32_32x32x16: for D = X Y, lane l supplies row (l & 31) of X and
+// column (l & 31) of Y, each as 8 consecutive k starting at 8*(l >> 5);
+// register r of the result holds D[8*(r>>2) + 4*(l>>5) + (r&3)][l & 31].
+// The kernels pass the B fragment as X and the A fragment as Y, so they
+// accumulate C^T: register r of lane l holds C[l & 31][8*(r>>2) + 4*(l>>5) +
+// (r&3)] -- four consecutive columns of one row per group of 4 registers,
+// which the epilogue writes as one 8- or 16-byte store.
 template <typename In>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
 template <>
@@ -90,41 +94,27 @@ __device__ __forceinline__ void lds_write16(TG_LDS char* base, uint32_t off, u32
 // 4 + (i >> 2), 8 + (i >> 2) and 12 + (i >> 2).  So if lane s addresses row
 // r0 + (s >> 2), columns c0 + 4*(s & 3) .. +3 of a row-major 16-bit tile,
 // lane i ends up with column c0 + i of rows r0 .. r0+3.
-//
-// It is issued through inline assembly: the compiler's own form of this read
-// makes it wait for every outstanding HBM->LDS copy first (vmcnt(0)), which
-// would drain the K pipeline at every step.  The caller therefore owns the
-// LDS wait: call lds_wait_tr() on the results before using them.
 __device__ __forceinline__ u32x2 lds_read_tr(const TG_LDS char* base, uint32_t off) {
-  u32x2 v;
-  const uint32_t addr = (uint32_t)(size_t)(base + off);
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
-  return v;
-}
-// Wait for this wave's LDS reads, then mark the fragments as produced after
-// the wait so that no consumer is scheduled ahead of it.
-template <int N>
-__device__ __forceinline__ void lds_wait_tr(u32x4 (&frag)[N]) {
-  asm volatile("s_waitcnt lgkmcnt(0)");
-#pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(frag[i]));
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS i16x4*)(base + off)));
 }
 
-// LDS swizzle, in 16-byte units.  A tile row is CH units long.
-//  * K-contiguous tiles (rows along M/N, CH = BK/8): fragment reads put 32
-//    lanes on 32 consecutive rows at one K offset; flipping the unit index by
-//    low row bits spreads each group of rows that shares a bank window.
+// LDS swizzle, in 16-byte units.  A tile row is CH units long.  gfx950's
+// LDS serves 256 bytes (64 banks) per clock, i.e. 16 lanes of a
+// ds_read_b128 or of a ds_read_b64_tr_b16 group pair per clock.
+//  * K-contiguous tiles (rows along M/N, CH = BK/8): a fragment read puts 16
+//    consecutive rows at one K offset in the same clock.  With W = 16/CH rows
+//    per 256-byte window, flipping the unit index by (row / W) makes those 16
+//    rows land on 16 distinct 16-byte slots.
 //  * M/N-contiguous tiles (rows along K): one transposing read has four rows
 //    at the same column offset per 16 lanes; flipping by a per-row pattern
 //    with distinct bits 1-2 and distinct bits 2-3 keeps those rows apart in
-//    both 128-byte and 256-byte bank windows.
+//    both 128-byte and 256-byte windows.
 template <bool KCONTIG, int CH>
 __device__ __forceinline__ uint32_t swz_unit(uint32_t row) {
   if constexpr (KCONTIG) {
-    if constexpr (CH >= 8)
-      return row & 7u;
-    else
-      return (row >> 1) & (uint32_t)(CH - 1);
+    static_assert(CH == 4 || CH == 8 || CH == 16, "K-contiguous rows of 32, 64 or 128 elements");
+    constexpr uint32_t shift = CH == 4 ? 2 : CH == 8 ? 1 : 0;
+    return (row >> shift) & (uint32_t)(CH - 1);
   } else {
     const uint32_t r = row & 3u;
     return ((r << 1) | ((r & 1u) << 3)) & (uint32_t)(CH - 1);
@@ -196,28 +186,27 @@ __device__ __forceinline__ void mma_stage(const TG_LDS char* sa, const TG_LDS ch
         bf[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
     }
-    if constexpr (!A_KC) lds_wait_tr(af);
-    if constexpr (!B_KC) lds_wait_tr(bf);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<In>(af[i], bf[j], acc[i][j]);
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<In>(bf[j], af[i], acc[i][j]);
   }
 }
 
-// Masked store of a wave's FM x FN 32x32 blocks (rows/cols past M/N dropped).
+// Element-wise masked store of a wave's FM x FN 32x32 blocks of C (any
+// alignment; rows/cols past M/N dropped).  acc[i][j] holds C^T (see above).
 template <typename Out, int FM, int FN>
 __device__ __forceinline__ void store_tile(void* Cb, int64_t ldc, int64_t M, int64_t N, int64_t r0, int64_t c0,
                                            int lane, const f32x16 (&acc)[FM][FN]) {
   const int li = lane & 31, lg = lane >> 5;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
+    const int64_t row = r0 + i * 32 + li;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int64_t col = c0 + j * 32 + li;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = r0 + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+        const int64_t col = c0 + j * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
         if (row < M && col < N) store_out<Out>(Cb, row * ldc + col, acc[i][j][r]);
       }
     }

@@ -63,7 +63,7 @@ bool vec_ok(const gemm_plan_t& p) {
   const int64_t b_contig = p.trans_b ? p.k : p.n;
   const int64_t span = (int64_t)1 << 30;  // 256 rows * ld * 2 bytes < 2^31
   return p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % 8 == 0 && a_contig % 8 == 0 && b_contig % 8 == 0 &&
-         a_contig >= 8 && b_contig >= 8 && p.lda * 256 < span && p.ldb * 256 < span;
+         a_contig >= 8 && b_contig >= 8 && p.lda * 256 < span && p.ldb * 256 < span && p.ldc * 512 < span;
 }
 
 bool skinny_ok(const gemm_plan_t& p) {
@@ -85,7 +85,7 @@ int skinny_choose(int64_t m, int64_t n) {
 int choose_tile(int64_t m, int64_t n) {
   auto tiles = [&](int t) { return cdiv(m, kTiles[t].bm) * cdiv(n, kTiles[t].bn); };
   if (m <= 32) return 5;
-  if (tiles(2) >= 512) return 2;  // 256x256: >= 2 work-groups per CU
+  if (tiles(8) >= 512) return 8;  // 256x256, 8 waves: >= 2 tiles per CU
   if (tiles(1) >= 256) return 1;  // 128x128
   return 0;                       // 64x64
 }

@@ -37,21 +37,50 @@
 
 #include "common.hpp"
 
+#include <type_traits>
+
 namespace tg {
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource for raw (unstructured) loads: 48-bit base, no stride,
+// `bytes` records (clamped below 2^31 so that kOutOfRange always misses), and
+// the gfx9 default data-format word.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
   const int32_t n = bytes > 0x7fffffff ? 0x7fffffff : (int32_t)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+  return i32x4{(int32_t)(uint32_t)a, (int32_t)((a >> 32) & 0xffffu), n, 0x00020000};
 }
 
-// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] in bits 3:0,
-// vmcnt[5:4] in bits 15:14, expcnt in 6:4 left at its maximum, lgkmcnt in
-// 11:8).  lgkmcnt(0) also retires this wave's LDS reads before a barrier
-// lets other waves overwrite the buffer they read.
-template <int N>
+// One wave-wide 16-byte-per-lane HBM->LDS copy: lane t's 16 bytes at
+// base + voff land at LDS byte address lds_addr + 16 t; offsets at or past
+// the resource's size read as zero.  Issued as inline assembly so that the
+// compiler neither waits on it before unrelated LDS reads nor reorders it
+// across the explicit waits below: the kernel counts these loads itself.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_addr)
+               : "m0");
+}
+
+// s_waitcnt vmcnt(N), optionally with lgkmcnt(0) (gfx9 encoding: vmcnt[3:0]
+// in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt in 6:4 left at its maximum,
+// lgkmcnt in 11:8).  lgkmcnt(0) retires this wave's LDS reads, needed when
+// the barrier that follows lets other waves overwrite the buffer just read.
+template <int N, bool LGKM0 = true>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (LGKM0 ? 0 : (0xF << 8)));
+}
+
+// Run-time count (0 .. 2 steps' worth of loads); the counter field is an
+// immediate, so dispatch over the few values a ring of <= 4 stages needs.
+template <int PER_STEP, bool LGKM0>
+__device__ __forceinline__ void wait_steps(int64_t steps) {
+  if (steps >= 2) wait_vmcnt<2 * PER_STEP, LGKM0>();
+  else if (steps == 1) wait_vmcnt<PER_STEP, LGKM0>();
+  else wait_vmcnt<0, LGKM0>();
 }
 
 // Work-group barrier that orders memory operations only at compile time; the
@@ -90,71 +119,231 @@ struct DmaOperand {
     }
   }
 
+  // Instruction i of this wave's share (0 <= i < IPW).
+  template <bool MASK_K>
+  __device__ __forceinline__ void issue_one(int i, const i32x4& rs, uint32_t tile_lds, int wave, int64_t k_left) const {
+    uint32_t off = voff[i];
+    if constexpr (MASK_K && KC) off = (int64_t)kofs[i] < k_left ? off : kOutOfRange;
+    dma16(rs, off, tile_lds + (uint32_t)(wave * IPW + i) * 1024u);
+  }
+
   // base: element (mn0, k0) [KC] or (k0, mn0) [MN]; bytes: from base to the
   // end of the matrix's last element; k_left = K - k0.
   template <bool MASK_K>
-  __device__ __forceinline__ void issue(const uint16_t* base, int64_t bytes, TG_LDS char* tile, int wave,
+  __device__ __forceinline__ void issue(const uint16_t* base, int64_t bytes, uint32_t tile_lds, int wave,
                                         int64_t k_left) const {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
+    const i32x4 rs = make_rsrc(base, bytes);
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       uint32_t off = voff[i];
       if constexpr (MASK_K && KC) off = (int64_t)kofs[i] < k_left ? off : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TG_LDS void*)(tile + (wave * IPW + i) * 1024), 16, off, 0, 0,
-                                               0);
+      dma16(rs, off, tile_lds + (uint32_t)(wave * IPW + i) * 1024u);
     }
   }
 };
 
-template <typename In, typename Out, int BM, int BN, int BK, int WM, int WN, int STAGES, bool TA, bool TB>
-__global__ void __launch_bounds__(WM * WN * 64) tile_gemm_kernel(GemmArgs args) {
+// ------------------------------------------------------------- epilogue ---
+// Stores go through the compiler's builtins (not inline assembly) so that its
+// hazard recognizer protects the store-data registers until they are read.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes > 0x7fffffff ? 0x7fffffff : (int32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t rs, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t rs, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, rs, (int)off, 0, 0);
+}
+template <typename Out>
+__device__ __forceinline__ uint32_t pack2(float a, float b);
+template <>
+__device__ __forceinline__ uint32_t pack2<__bf16>(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});  // nearest, ties to even
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<_Float16>(float a, float b) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, f16x2{(_Float16)a, (_Float16)b});
+}
+
+// Vector store of a wave's FM x FN 32x32 blocks of C (acc holds C^T): every
+// group of four registers is four consecutive columns of one row, written as
+// one 16-byte (fp32) or 8-byte (16-bit) buffer store.  The descriptor's size
+// ends at the last element of C, which drops rows past M; groups at or past
+// column N get an out-of-range offset.  Needs N % 4 == 0 or a tile that ends
+// inside N (the caller falls back to store_tile otherwise).
+template <typename Out, int FM, int FN>
+__device__ __forceinline__ void store_tile_vec(const void* Ctile, int64_t bytes, int64_t ldc, int64_t n_left,
+                                               int lane, const f32x16 (&acc)[FM][FN]) {
+  const __amdgpu_buffer_rsrc_t rs = store_rsrc(Ctile, bytes);
+  const int li = lane & 31, lg = lane >> 5;
+  constexpr uint32_t es = sizeof(Out);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const uint32_t rowoff = (uint32_t)((i * 32 + li) * ldc) * es;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = j * 32 + 8 * g + 4 * lg;
+        const uint32_t off = col < n_left ? rowoff + (uint32_t)col * es : kOutOfRange;
+        const f32x16& a = acc[i][j];
+        if constexpr (sizeof(Out) == 4) {
+          // (bit-cast the 4-vector as a whole: this compiler mislowers a bit
+          // cast of a single vector element)
+          buf_store16(rs, off, __builtin_bit_cast(u32x4, f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]}));
+        } else {
+          buf_store8(rs, off, u32x2{pack2<Out>(a[4 * g], a[4 * g + 1]), pack2<Out>(a[4 * g + 2], a[4 * g + 3])});
+        }
+      }
+    }
+  }
+}
+
+// Fragments of one 16-deep K slice for a wave's FM x FN blocks.
+template <int FM, int FN>
+struct Frags {
+  u32x4 a[FM], b[FN];
+};
+
+template <typename In, typename Out, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int DW, bool TA, bool TB>
+__global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_kernel(GemmArgs args) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BK % 16 == 0 && STAGES >= 2, "tile shape");
+  constexpr int KS = BK / 16;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BK % 32 == 0 && STAGES >= 2 && STAGES <= 5, "tile shape");
   constexpr bool A_KC = !TA, B_KC = TB;
-  using OA = DmaOperand<A_KC, BM, BK, NW>;
-  using OB = DmaOperand<B_KC, BN, BK, NW>;
+  // The last DW waves issue every HBM->LDS copy; with DW < NW the other waves
+  // never stall on the texture path and keep the matrix cores fed.
+  static_assert(DW >= 1 && DW <= NW, "copy waves");
+  using OA = DmaOperand<A_KC, BM, BK, DW>;
+  using OB = DmaOperand<B_KC, BN, BK, DW>;
   constexpr uint32_t A_BYTES = OA::BYTES, STAGE = OA::BYTES + OB::BYTES;
-  constexpr int PER_STEP = OA::IPW + OB::IPW;  // vector-memory ops per wave per K step
+  constexpr int PER_STEP = OA::IPW + OB::IPW;  // copy instructions per copy wave per K step
+  constexpr int READS = FM * (A_KC ? 1 : 2) + FN * (B_KC ? 1 : 2);  // LDS reads per 16-deep slice
+  constexpr int MMAS = FM * FN;
+  // Ring schedule.  A barrier at the start of every stage's last 16-deep
+  // slice publishes stage kt + 1 (each wave first waits for its own copies),
+  // and the copies for a later stage are interleaved with that slice's MFMAs.
+  //  * With three or more buffers (EARLY) stage kt + STAGES - 1 goes into the
+  //    buffer of stage kt - 1: every wave finished reading it before this
+  //    barrier, so the barrier need not wait for this wave's own LDS reads.
+  //  * With two buffers stage kt + 2 reuses stage kt's buffer, and the
+  //    barrier must first retire this wave's reads of stage kt.
+  constexpr bool EARLY = STAGES >= 3;
+  constexpr int D = EARLY ? STAGES - 1 : STAGES;
 
   extern __shared__ __attribute__((aligned(1024))) char tg_smem[];
   TG_LDS char* lds = (TG_LDS char*)tg_smem;
+  const uint32_t lds0 = (uint32_t)(size_t)lds;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
+  const int li = lane & 31, lg = lane >> 5;
+  const int trh = lane >> 4, trs = lane & 15;
 
   int32_t pm, pn;
   tile_coords<8>(blockIdx.x, args.tiles_m, args.tiles_n, pm, pn);
   const int64_t m0 = (int64_t)pm * BM, n0 = (int64_t)pn * BN;
   const int64_t M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
 
+  const int dwave = wave - (NW - DW);  // index among the copy waves (< 0: computes only)
+  const bool copier = dwave >= 0;
   OA oa;
   OB ob;
-  oa.init(wave, lane, lda);
-  ob.init(wave, lane, ldb);
+  oa.init(copier ? dwave : 0, lane, lda);
+  ob.init(copier ? dwave : 0, lane, ldb);
+
+  // Per-lane LDS byte offsets of this wave's fragment reads for every slice
+  // of a stage (the stage base is a compile-time immediate in steady state).
+  uint32_t offa[KS][FM], offb[KS][FN];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int rb = wm0 + i * 32;
+      if constexpr (A_KC)
+        offa[ks][i] = swz_off<true, OA::CH>(rb + li, ks * 16 + lg * 8);
+      else
+        offa[ks][i] = swz_off<false, OA::CH>(ks * 16 + 8 * (trh >> 1) + (trs >> 2), rb + 16 * (trh & 1) + 4 * (trs & 3));
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int cb = wn0 + j * 32;
+      if constexpr (B_KC)
+        offb[ks][j] = A_BYTES + swz_off<true, OB::CH>(cb + li, ks * 16 + lg * 8);
+      else
+        offb[ks][j] = A_BYTES + swz_off<false, OB::CH>(ks * 16 + 8 * (trh >> 1) + (trs >> 2),
+                                                       cb + 16 * (trh & 1) + 4 * (trs & 3));
+    }
+  }
+  // the second transposing read of a fragment is 4 rows further down
+  constexpr uint32_t A_TR4 = 4 * OA::CH * 16, B_TR4 = 4 * OB::CH * 16;
 
   const int64_t nk = (K + BK - 1) / BK, nfull = K / BK;
+  // bytes the loads of one operand advance per K step
+  const int64_t a_step = A_KC ? (int64_t)BK * 2 : (int64_t)BK * lda * 2;
+  const int64_t b_step = B_KC ? (int64_t)BK * 2 : (int64_t)BK * ldb * 2;
 
   for (int64_t b = blockIdx.y; b < args.batch; b += gridDim.y) {
-    const uint16_t* Ab = args.A + b * args.sA;
-    const uint16_t* Bb = args.B + b * args.sB;
+    // running source pointers / remaining bytes of the next step to load
+    const char* a_ptr = (const char*)(args.A + b * args.sA + (A_KC ? m0 * lda : m0));
+    const char* b_ptr = (const char*)(args.B + b * args.sB + (B_KC ? n0 * ldb : n0));
+    int64_t a_left = A_KC ? ((M - 1 - m0) * lda + K) * 2 : ((K - 1) * lda + (M - m0)) * 2;
+    int64_t b_left = B_KC ? ((N - 1 - n0) * ldb + K) * 2 : ((K - 1) * ldb + (N - n0)) * 2;
+    int64_t k_left = K;  // K - k0 of the next step to load
 
-    auto issue = [&](int64_t kt) {
-      const int64_t k0 = kt * BK;
-      TG_LDS char* st = lds + (uint32_t)(kt % STAGES) * STAGE;
-      const uint16_t* a0 = A_KC ? Ab + m0 * lda + k0 : Ab + k0 * lda + m0;
-      const int64_t abytes = A_KC ? ((M - 1 - m0) * lda + (K - k0)) * 2 : ((K - 1 - k0) * lda + (M - m0)) * 2;
-      const uint16_t* b0 = B_KC ? Bb + n0 * ldb + k0 : Bb + k0 * ldb + n0;
-      const int64_t bbytes = B_KC ? ((N - 1 - n0) * ldb + (K - k0)) * 2 : ((K - 1 - k0) * ldb + (N - n0)) * 2;
-      if (kt < nfull) {
-        oa.template issue<false>(a0, abytes, st, wave, K - k0);
-        ob.template issue<false>(b0, bbytes, st + A_BYTES, wave, K - k0);
+    auto issue = [&](uint32_t buf, auto full) {
+      const uint32_t st = lds0 + buf * STAGE;
+      if (!copier) {
+      } else if (decltype(full)::value || k_left >= BK) {
+        oa.template issue<false>((const uint16_t*)a_ptr, a_left, st, dwave, k_left);
+        ob.template issue<false>((const uint16_t*)b_ptr, b_left, st + A_BYTES, dwave, k_left);
       } else {
-        oa.template issue<true>(a0, abytes, st, wave, K - k0);
-        ob.template issue<true>(b0, bbytes, st + A_BYTES, wave, K - k0);
+        oa.template issue<true>((const uint16_t*)a_ptr, a_left, st, dwave, k_left);
+        ob.template issue<true>((const uint16_t*)b_ptr, b_left, st + A_BYTES, dwave, k_left);
       }
+      a_ptr += a_step;
+      a_left -= a_step;
+      b_ptr += b_step;
+      b_left -= b_step;
+      k_left -= BK;
+    };
+
+    // LDS -> registers: read r (0 <= r < READS) of slice ks of the stage at
+    // byte `base`; A fragments first, then B, two transposing reads per
+    // M/N-contiguous fragment.
+    auto read_one = [&](uint32_t base, int ks, int r, Frags<FM, FN>& f) {
+      const TG_LDS char* sb = lds + base;
+      constexpr int RA = FM * (A_KC ? 1 : 2);
+      if (r < RA) {
+        if constexpr (A_KC) {
+          f.a[r] = lds_read16(sb, offa[ks][r]);
+        } else {
+          const int i = r >> 1;
+          const u32x2 v = lds_read_tr(sb, offa[ks][i] + ((r & 1) ? A_TR4 : 0u));
+          f.a[i][(r & 1) * 2] = v[0];
+          f.a[i][(r & 1) * 2 + 1] = v[1];
+        }
+      } else {
+        const int q = r - RA;
+        if constexpr (B_KC) {
+          f.b[q] = lds_read16(sb, offb[ks][q]);
+        } else {
+          const int j = q >> 1;
+          const u32x2 v = lds_read_tr(sb, offb[ks][j] + ((q & 1) ? B_TR4 : 0u));
+          f.b[j][(q & 1) * 2] = v[0];
+          f.b[j][(q & 1) * 2 + 1] = v[1];
+        }
+      }
+    };
+    auto read = [&](uint32_t base, int ks, Frags<FM, FN>& f) {
+#pragma unroll
+      for (int r = 0; r < READS; ++r) read_one(base, ks, r, f);
     };
 
     f32x16 acc[FM][FN];
@@ -165,31 +354,127 @@ __global__ void __launch_bounds__(WM * WN * 64) tile_gemm_kernel(GemmArgs args) 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    // One 16-deep slice in a fixed instruction order: MFMA m, then the m-th
+    // LDS read for the next slice, then (evenly spaced) one HBM->LDS copy of
+    // this wave's instructions [d0, d0 + cnt) for a later stage, so that
+    // neither the LDS nor the vector-memory path sees a burst.
+    // sched_barrier(0) pins the order.
+    auto dma_one = [&](int d, const i32x4& ra, const i32x4& rb, uint32_t dst) {
+      if (!copier) return;
+      if (d < OA::IPW)
+        oa.template issue_one<false>(d, ra, dst, dwave, BK);
+      else
+        ob.template issue_one<false>(d - OA::IPW, rb, dst + A_BYTES, dwave, BK);
+    };
+    auto slice = [&](const Frags<FM, FN>& cur, Frags<FM, FN>* nxt, uint32_t nbase, int nks, const i32x4* rsa,
+                     const i32x4* rsb, uint32_t dma_st, int d0, int cnt) {
+      const int every = cnt > 0 ? (MMAS / cnt > 0 ? MMAS / cnt : 1) : MMAS;
+      int d = 0;
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-      if (s < nk) issue(s);
-
-    for (int64_t kt = 0; kt < nk; ++kt) {
-      // loads issued after step kt that may stay in flight
-      const int64_t ahead = min((int64_t)(STAGES - 2), nk - 1 - kt);
-      if constexpr (STAGES >= 4) {
-        if (ahead >= 2) wait_vmcnt<2 * PER_STEP>();
-        else if (ahead == 1) wait_vmcnt<PER_STEP>();
-        else wait_vmcnt<0>();
-      } else if constexpr (STAGES == 3) {
-        if (ahead >= 1) wait_vmcnt<PER_STEP>();
-        else wait_vmcnt<0>();
-      } else {
-        wait_vmcnt<0>();
+      for (int m = 0; m < MMAS; ++m) {
+        const int i = m / FN, j = m % FN;
+        acc[i][j] = mfma32<In>(cur.b[j], cur.a[i], acc[i][j]);
+        if (nxt && m < READS) read_one(nbase, nks, m, *nxt);
+        if (rsa && m % every == every - 1 && d < cnt) {
+          dma_one(d0 + d, *rsa, *rsb, dma_st);
+          ++d;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      if (nxt) {
+#pragma unroll
+        for (int r = MMAS; r < READS; ++r) read_one(nbase, nks, r, *nxt);
+      }
+      if (rsa) {
+#pragma unroll
+        for (; d < cnt; ++d) dma_one(d0 + d, *rsa, *rsb, dma_st);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto mma = [&](const Frags<FM, FN>& f) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<In>(f.b[j], f.a[i], acc[i][j]);
+    };
+
+    if (nk > 0) {
+      Frags<FM, FN> f[2];
+#pragma unroll
+      for (int s = 0; s < D; ++s)
+        if (s < nk) issue((uint32_t)s, std::false_type{});
+      wait_steps<PER_STEP, true>(min((int64_t)D, nk) - 1);
       block_barrier();
-      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
-      const TG_LDS char* sa = lds + (uint32_t)(kt % STAGES) * STAGE;
-      mma_stage<In, FM, FN, BK, A_KC, B_KC, OA::CH, OB::CH>(sa, sa + A_BYTES, wm0, wn0, lane, acc);
+      read(0, 0, f[0]);
+
+      // One stage held in buffer `buf`: KS slices; the last slice crosses to
+      // the next stage after the wait + barrier that publishes stage kt + 1.
+      auto stage_const = [&](auto bufc) {
+        constexpr uint32_t buf = decltype(bufc)::value;
+        constexpr uint32_t dst = ((buf + D) % STAGES) * STAGE;
+        const i32x4 rsa = make_rsrc(a_ptr, a_left), rsb = make_rsrc(b_ptr, b_left);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          Frags<FM, FN>& cur = f[ks & 1];
+          Frags<FM, FN>& nxt = f[(ks & 1) ^ 1];
+          if (ks + 1 < KS) {
+            slice(cur, &nxt, buf * STAGE, ks + 1, nullptr, nullptr, 0, 0, 0);
+          } else {
+            // copies for stages kt+2 .. kt+D-1 may stay in flight
+            wait_vmcnt<(D - 2) * PER_STEP, !EARLY>();
+            block_barrier();
+            slice(cur, &nxt, ((buf + 1) % STAGES) * STAGE, 0, &rsa, &rsb, lds0 + dst, 0, PER_STEP);
+          }
+        }
+        a_ptr += a_step;
+        a_left -= a_step;
+        b_ptr += b_step;
+        b_left -= b_step;
+        k_left -= BK;
+      };
+      auto stage_dyn = [&](int64_t kt) {
+        const uint32_t buf = (uint32_t)(kt % STAGES);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          Frags<FM, FN>& cur = f[ks & 1];
+          Frags<FM, FN>& nxt = f[(ks & 1) ^ 1];
+          if (ks + 1 < KS) {
+            read(buf * STAGE, ks + 1, nxt);
+          } else if (kt + 1 < nk) {
+            wait_steps<PER_STEP, !EARLY>(min((int64_t)(D - 2), nk - 2 - kt));
+            block_barrier();
+            if (kt + D < nk) issue((uint32_t)((kt + D) % STAGES), std::false_type{});
+            read((uint32_t)((kt + 1) % STAGES) * STAGE, 0, nxt);
+          }
+          mma(cur);
+        }
+      };
+      // steady state: groups of STAGES stages (compile-time buffers) whose
+      // loads are all full K steps
+      const int64_t nsteady = max((int64_t)0, min(nk, nfull) - D);
+      int64_t kt = 0;
+      for (; kt + STAGES <= nsteady; kt += STAGES) {
+        stage_const(std::integral_constant<uint32_t, 0>{});
+        stage_const(std::integral_constant<uint32_t, 1>{});
+        if constexpr (STAGES > 2) stage_const(std::integral_constant<uint32_t, 2>{});
+        if constexpr (STAGES > 3) stage_const(std::integral_constant<uint32_t, 3>{});
+        if constexpr (STAGES > 4) stage_const(std::integral_constant<uint32_t, 4>{});
+      }
+      for (; kt < nk; ++kt) stage_dyn(kt);
     }
 
-    void* Cb = (char*)args.C + b * args.sC * (int64_t)sizeof(Out);
-    store_tile<Out, FM, FN>(Cb, args.ldc, M, N, m0 + wm0, n0 + wn0, lane, acc);
+    {
+      const int64_t r0 = m0 + wm0, c0 = n0 + wn0;
+      char* Cb = (char*)args.C + b * args.sC * (int64_t)sizeof(Out);
+      if (N % 4 == 0 || n0 + BN <= N) {
+        if (r0 < M && c0 < N)
+          store_tile_vec<Out, FM, FN>(Cb + (r0 * args.ldc + c0) * (int64_t)sizeof(Out),
+                                      ((M - 1 - r0) * args.ldc + (N - c0)) * (int64_t)sizeof(Out), args.ldc, N - c0,
+                                      lane, acc);
+      } else {
+        store_tile<Out, FM, FN>(Cb, args.ldc, M, N, r0, c0, lane, acc);
+      }
+    }
     if (b + gridDim.y < args.batch) {
       // the next matrix's prologue overwrites buffers other waves may still read
       wait_vmcnt<0>();

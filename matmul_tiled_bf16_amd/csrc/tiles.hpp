@@ -11,6 +11,8 @@ namespace tg {
 
 struct TileShape {
   int bm, bn, bk, wm, wn, stages;
+  int occ = 1;  // work-groups meant to share one CU (register/LDS budget per wave follows)
+  int dw = 0;   // waves that issue the HBM->LDS copies (0: all of them)
 };
 
 constexpr TileShape kTiles[] = {
@@ -22,6 +24,16 @@ constexpr TileShape kTiles[] = {
     {32, 128, 64, 1, 4, 2},    // 5: one 32-row tile -- thin M
     {128, 128, 32, 2, 2, 4},   // 6: 64x64 per wave, 4-deep ring
     {256, 256, 64, 2, 2, 2},   // 7: 128x128 per wave, 2-deep ring
+    {256, 256, 32, 2, 4, 4},   // 8: 8 waves (2 per SIMD), 128x64 per wave, 4-deep ring
+    {256, 256, 64, 2, 4, 2},   // 9: 8 waves, 128x64 per wave, 2-deep ring
+    // two work-groups per CU (<= 80 KiB LDS, <= 256 registers per lane each)
+    {256, 128, 32, 2, 2, 3, 2},  // 10: 128x64 per wave, 3-deep ring
+    {128, 256, 32, 2, 2, 3, 2},  // 11: 64x128 per wave, 3-deep ring
+    {256, 128, 32, 2, 2, 2, 2},  // 12: 128x64 per wave, 2-deep ring
+    {128, 128, 64, 2, 2, 2, 2},  // 13: 64x64 per wave
+    // 8 waves, copies issued by the second wave of each SIMD only
+    {256, 256, 64, 2, 4, 2, 1, 4},  // 14
+    {256, 256, 32, 2, 4, 4, 1, 4},  // 15
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 

@@ -129,7 +129,7 @@ def test_plan_choices_for_the_workloads():
     p = tg.plan(2048, 128, 2048)
     assert p.variant == tg.VARIANT_TILE
     p = tg.plan(8192, 8192, 8192, out_dtype=torch.bfloat16)
-    assert (p.variant, p.bm, p.bn) == (tg.VARIANT_TILE, 256, 256) and p.tiles_m * p.tiles_n == 1024
+    assert (p.variant, p.bm, p.bn, p.wg_threads) == (tg.VARIANT_TILE, 256, 256, 512) and p.tiles_m * p.tiles_n == 1024
     assert p.workspace_bytes == 0
 
 

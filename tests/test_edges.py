@@ -121,7 +121,7 @@ def test_integer_inputs_are_bit_exact(out_dtype, ta, tb):
 def test_every_tile_gives_the_same_answer():
     """Block parameters must never change the output: all tile shapes agree with
     the oracle, and bit for bit with each other on integer inputs."""
-    shapes = [(tg.VARIANT_TILE, t) for t in range(8)] + [(tg.VARIANT_GENERIC, t) for t in range(2)]
+    shapes = [(tg.VARIANT_TILE, t) for t in range(16)] + [(tg.VARIANT_GENERIC, t) for t in range(2)]
     for ta, tb in [(0, 0), (1, 1), (0, 1), (1, 0)]:
         ref_bits = None
         for variant, tile in shapes:
