@@ -68,6 +68,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile", type=int, default=None, help="override the planner's tile (same variant)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (to calibrate FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -78,7 +80,16 @@ def main():
 
     import torch
     import matmul_tiled_bf16_amd as tg
-    from matmul_tiled_bf16_amd import roofline
+    from matmul_tiled_bf16_amd import profiling, roofline
+
+    if args.copy_calibration:
+        src = torch.empty(profiling.COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": profiling.COPY_BYTES, "copies": 4}))
+        return
 
     (p,) = problems(args.workload)
     dev = torch.device("cuda:0")
@@ -164,7 +175,7 @@ def main():
         "gbps": round(gbps, 1),
         "pct_hbm_peak": round(100 * nbytes / (ms_per_step / 1e3) / PEAK_HBM, 2),
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": runit,
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4), "traffic": profiling.read_traffic(p.name),
                      "kernel_ms": round(kernel_s * 1e3, 5),
                      "algorithmic": {"flops": flops, "bytes": nbytes}},
     }
