@@ -116,7 +116,7 @@ def main():
         pl = tg.plan(p.m, p.n, p.k, trans_a=p.trans_a, trans_b=p.trans_b, in_dtype=tin, out_dtype=tout,
                      lda=p.lda, ldb=p.ldb, ldc=p.ldc)
         if args.tile is not None:
-            pl.tile = args.tile
+            pl.tile = args.tile  # same variant; the launcher re-validates it
         B = Bs[i % len(Bs)]
         C = Cs[i % len(Cs)]
         if p.batch == 1:
@@ -139,10 +139,16 @@ def main():
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    kernel_s = float(np.mean(kms)) / 1e3
+    timed_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms_per_step = wall * 1e3 / args.steps
     assert torch.isfinite(Cs[0].float()).all().item(), "non-finite output"
+
+    # Kernel durations: the same launches, queued while the stream is held by a
+    # GPU-side sleep, so that host time between launches (plan, marshalling)
+    # cannot show up between the events.  For launches longer than the host's
+    # per-step time this equals the timed region's own per-launch events.
+    mean_ms, kms, queued_ahead = gated_kernel_ms(torch, stream, step, args.steps, max(args.warmup, 1))
+    kernel_s = mean_ms / 1e3
 
     tflops = flops / (ms_per_step / 1e3) / 1e12
     gbps = nbytes / (ms_per_step / 1e3) / 1e9
@@ -169,7 +175,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": p.name, "m": p.m, "n": p.n, "k": p.k, "batch": p.batch, "op": trans,
                    "in_dtype": p.in_dtype, "out_dtype": p.out_dtype, "b_copies": len(Bs),
-                   "variant": int(pl.variant), "tile": [int(pl.bm), int(pl.bn), int(pl.bk)]},
+                   "variant": int(pl.variant), "tile_index": int(pl.tile)},
         "tflops": round(tflops, 2),
         "pct_mfma_peak": round(100 * flops / (ms_per_step / 1e3) / PEAK_MFMA, 2),
         "gbps": round(gbps, 1),
@@ -177,11 +183,70 @@ def main():
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": runit,
                      "frac": round(achieved / peak, 4), "traffic": profiling.read_traffic(p.name),
                      "kernel_ms": round(kernel_s * 1e3, 5),
+                     "kernel_ms_each_min": round(float(np.min(kms)), 5),
+                     "kernel_ms_each_p90": round(float(np.percentile(kms, 90)), 5),
+                     "kernel_ms_timed_region": round(float(np.mean(timed_ms)), 5),
+                     "launches_queued_ahead": bool(queued_ahead),
                      "algorithmic": {"flops": flops, "bytes": nbytes}},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(p, unit, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def _held(torch, stream, enqueue):
+    """Run enqueue() while the stream is held by a GPU-side sleep, so that the
+    host finishes queueing before the GPU starts; retried with a longer sleep
+    if the sleep ran out first.  Returns whether the queue stayed ahead."""
+    woke = torch.cuda.Event()
+    cycles = 20_000_000
+    for _attempt in range(4):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(cycles)
+        woke.record(stream)
+        enqueue()
+        ahead = not woke.query()
+        torch.cuda.synchronize()
+        if ahead:
+            return True
+        cycles *= 4
+    return False
+
+
+def gated_kernel_ms(torch, stream, step, n, warm):
+    """Kernel durations with host overhead kept out of the GPU timeline.
+
+    Returns (mean ms per launch from one event pair around n back-to-back
+    launches, per-launch ms from an event pair around each launch, whether
+    the queue stayed ahead of the GPU in both passes).  The first figure is
+    the kernel's own time (plus the sub-microsecond launch-to-launch gap);
+    per-launch event pairs add a few microseconds of their own to each
+    launch, so they serve only for the spread (min, p90)."""
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def batch():
+        for i in range(warm):  # clocks ramp back up after the sleep
+            step(i)
+        t0.record(stream)
+        for i in range(n):
+            step(i)
+        t1.record(stream)
+
+    ahead_b = _held(torch, stream, batch)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    def each():
+        for i in range(warm):
+            step(i)
+        for i in range(n):
+            starts[i].record(stream)
+            step(i)
+            ends[i].record(stream)
+
+    ahead_e = _held(torch, stream, each)
+    return t0.elapsed_time(t1) / n, [s.elapsed_time(e) for s, e in zip(starts, ends)], ahead_b and ahead_e
 
 
 def cpu_baseline(p, unit, seconds):

@@ -131,6 +131,14 @@ const char* tg_status_str(tg_status s);
 /* TG_ABI_VERSION of the built library, to detect a header/library mismatch. */
 int32_t tg_abi_version(void);
 
+/*
+ * Number of tile shapes the library holds for `variant` (one of tg_variant);
+ * valid `tile` values in a caller-overridden plan are 0 .. count-1.  Returns
+ * 0 for an unknown variant.  Every shape yields the same result up to the
+ * order of fp32 additions (for integer-valued inputs, bit-identical).
+ */
+int32_t tg_variant_tiles(int32_t variant);
+
 #ifdef __cplusplus
 }
 #endif

@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.tg_status_str.argtypes = [ctypes.c_int]
         L.tg_abi_version.restype = i32
         L.tg_abi_version.argtypes = []
+        L.tg_variant_tiles.restype = i32
+        L.tg_variant_tiles.argtypes = [i32]
         if L.tg_abi_version() != _abi_version_from_header():
             raise RuntimeError("libtgemm.so was built from a different tgemm.h (ABI version mismatch)")
         _lib = L
@@ -89,6 +91,11 @@ def lib() -> ctypes.CDLL:
 
 def status_str(s: int) -> str:
     return lib().tg_status_str(int(s)).decode()
+
+
+def variant_tiles(variant: int) -> int:
+    """Number of tile shapes the library holds for `variant` (valid plan.tile values)."""
+    return int(lib().tg_variant_tiles(variant))
 
 
 def _dtype_code(dt) -> int:

@@ -1,5 +1,8 @@
 // inst_skinny.hip -- instances of the skinny (M <= 32) streaming kernel for
-// every (input type, output type) pair.
+// every (input type, output type) pair and every shape in kSkinny.
+#include <array>
+#include <utility>
+
 #include "tiles.hpp"
 #include "skinny_gemm.hpp"
 
@@ -9,22 +12,23 @@ namespace {
 template <typename In, typename Out, int T>
 constexpr KernelFn skinny_k() {
   constexpr SkinnyShape s = kSkinny[T];
-  return &skinny_gemm_kernel<In, Out, s.mb, s.nblk, s.waves, s.unroll>;
+  return &skinny_gemm_kernel<In, Out, s.mb, s.nb, s.waves, s.stages, s.sk>;
+}
+
+template <typename In, typename Out, std::size_t... I>
+constexpr std::array<KernelFn, sizeof...(I)> skinny_array(std::index_sequence<I...>) {
+  return {skinny_k<In, Out, I>()...};
+}
+template <typename In, typename Out>
+constexpr std::array<KernelFn, kNumSkinny> row() {
+  return skinny_array<In, Out>(std::make_index_sequence<kNumSkinny>{});
 }
 
 }  // namespace
 
-extern const KernelFn skinny_table[2][2][kNumSkinny];
-// [input bf16/fp16][output fp32/same]
-const KernelFn skinny_table[2][2][kNumSkinny] = {
-    {{skinny_k<__bf16, float, 0>(), skinny_k<__bf16, float, 1>(), skinny_k<__bf16, float, 2>(),
-      skinny_k<__bf16, float, 3>()},
-     {skinny_k<__bf16, __bf16, 0>(), skinny_k<__bf16, __bf16, 1>(), skinny_k<__bf16, __bf16, 2>(),
-      skinny_k<__bf16, __bf16, 3>()}},
-    {{skinny_k<_Float16, float, 0>(), skinny_k<_Float16, float, 1>(), skinny_k<_Float16, float, 2>(),
-      skinny_k<_Float16, float, 3>()},
-     {skinny_k<_Float16, _Float16, 0>(), skinny_k<_Float16, _Float16, 1>(), skinny_k<_Float16, _Float16, 2>(),
-      skinny_k<_Float16, _Float16, 3>()}}};
-static_assert(kNumSkinny == 4, "update the skinny instance table");
+// [input bf16/fp16][output fp32/same][shape]
+extern const std::array<KernelFn, kNumSkinny> skinny_table[2][2];
+const std::array<KernelFn, kNumSkinny> skinny_table[2][2] = {{row<__bf16, float>(), row<__bf16, __bf16>()},
+                                                            {row<_Float16, float>(), row<_Float16, _Float16>()}};
 
 }  // namespace tg

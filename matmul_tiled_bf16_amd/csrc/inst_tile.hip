@@ -3,6 +3,9 @@
 //   TG_IN, TG_OUT (element types), TG_TA, TG_TB (0/1) and
 //   TG_TABLE_TILE, TG_TABLE_GENERIC (names of the exported tables).
 // The library compiles this file once per combination.
+#include <array>
+#include <utility>
+
 #include "tiles.hpp"
 #include "tile_gemm.hpp"
 #include "generic_gemm.hpp"
@@ -23,17 +26,20 @@ constexpr KernelFn generic_k() {
   return &generic_gemm_kernel<TG_IN, TG_OUT, s.bm, s.bn, s.bk, s.wm, s.wn, TG_TA != 0, TG_TB != 0>;
 }
 
+template <std::size_t... I>
+constexpr std::array<KernelFn, sizeof...(I)> tile_array(std::index_sequence<I...>) {
+  return {tile_k<I>()...};
+}
+template <std::size_t... I>
+constexpr std::array<KernelFn, sizeof...(I)> generic_array(std::index_sequence<I...>) {
+  return {generic_k<I>()...};
+}
+
 }  // namespace
 
-extern const KernelFn TG_TABLE_TILE[kNumTiles];
-extern const KernelFn TG_TABLE_GENERIC[kNumGeneric];
-
-#define TG_TILE_ENTRY(i) tile_k<i>()
-const KernelFn TG_TABLE_TILE[kNumTiles] = {TG_TILE_ENTRY(0), TG_TILE_ENTRY(1), TG_TILE_ENTRY(2), TG_TILE_ENTRY(3),
-                                          TG_TILE_ENTRY(4), TG_TILE_ENTRY(5), TG_TILE_ENTRY(6), TG_TILE_ENTRY(7),
-                                          TG_TILE_ENTRY(8), TG_TILE_ENTRY(9), TG_TILE_ENTRY(10), TG_TILE_ENTRY(11),
-                                          TG_TILE_ENTRY(12), TG_TILE_ENTRY(13), TG_TILE_ENTRY(14), TG_TILE_ENTRY(15)};
-const KernelFn TG_TABLE_GENERIC[kNumGeneric] = {generic_k<0>(), generic_k<1>()};
-static_assert(kNumTiles == 16 && kNumGeneric == 2, "update the instance tables");
+extern const std::array<KernelFn, kNumTiles> TG_TABLE_TILE;
+extern const std::array<KernelFn, kNumGeneric> TG_TABLE_GENERIC;
+const std::array<KernelFn, kNumTiles> TG_TABLE_TILE = tile_array(std::make_index_sequence<kNumTiles>{});
+const std::array<KernelFn, kNumGeneric> TG_TABLE_GENERIC = generic_array(std::make_index_sequence<kNumGeneric>{});
 
 }  // namespace tg

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <array>
+
 #include "../../include/tgemm.h"
 #include "common.hpp"
 #include "tiles.hpp"
@@ -17,16 +19,16 @@
 namespace tg {
 // Instance tables, one per (input, output, trans_a, trans_b); defined by the
 // objects built from inst_tile.hip and inst_skinny.hip.
-#define TG_DECLARE(in, out, ta, tb)                                  \
-  extern const KernelFn tile_##in##_##out##_##ta##tb[kNumTiles];     \
-  extern const KernelFn generic_##in##_##out##_##ta##tb[kNumGeneric];
+#define TG_DECLARE(in, out, ta, tb)                                                \
+  extern const std::array<KernelFn, kNumTiles> tile_##in##_##out##_##ta##tb;       \
+  extern const std::array<KernelFn, kNumGeneric> generic_##in##_##out##_##ta##tb;
 #define TG_DECLARE_IO(in, out) \
   TG_DECLARE(in, out, 0, 0) TG_DECLARE(in, out, 0, 1) TG_DECLARE(in, out, 1, 0) TG_DECLARE(in, out, 1, 1)
 TG_DECLARE_IO(bf16, f32)
 TG_DECLARE_IO(bf16, bf16)
 TG_DECLARE_IO(f16, f32)
 TG_DECLARE_IO(f16, f16)
-extern const KernelFn skinny_table[2][2][kNumSkinny];
+extern const std::array<KernelFn, kNumSkinny> skinny_table[2][2];
 }  // namespace tg
 
 namespace {
@@ -40,11 +42,12 @@ using tg::kSkinny;
 using tg::kTiles;
 using tg::TileShape;
 
-#define TG_ROW(in, out) \
-  {tg::tile_##in##_##out##_00, tg::tile_##in##_##out##_01, tg::tile_##in##_##out##_10, tg::tile_##in##_##out##_11}
-#define TG_GROW(in, out)                                                                              \
-  {tg::generic_##in##_##out##_00, tg::generic_##in##_##out##_01, tg::generic_##in##_##out##_10, \
-   tg::generic_##in##_##out##_11}
+#define TG_ROW(in, out)                                                                           \
+  {tg::tile_##in##_##out##_00.data(), tg::tile_##in##_##out##_01.data(), tg::tile_##in##_##out##_10.data(), \
+   tg::tile_##in##_##out##_11.data()}
+#define TG_GROW(in, out)                                                                                      \
+  {tg::generic_##in##_##out##_00.data(), tg::generic_##in##_##out##_01.data(),                              \
+   tg::generic_##in##_##out##_10.data(), tg::generic_##in##_##out##_11.data()}
 
 // [in bf16/fp16][out fp32/same][2*trans_a + trans_b]
 const KernelFn* const kTileTables[2][2][4] = {{TG_ROW(bf16, f32), TG_ROW(bf16, bf16)},
@@ -66,17 +69,18 @@ bool vec_ok(const gemm_plan_t& p) {
          a_contig >= 8 && b_contig >= 8 && p.lda * 256 < span && p.ldb * 256 < span && p.ldc * 512 < span;
 }
 
+// The skinny kernel reads 16-byte chunks of A's and B's rows along K through
+// buffer descriptors whose 31-bit byte offsets span one work-group's rows of
+// B (at most 64) or all of A (at most 32 rows), plus the K extent.
 bool skinny_ok(const gemm_plan_t& p) {
+  const int64_t lim = (int64_t)1 << 31;
   return !p.trans_a && p.trans_b && p.m >= 1 && p.m <= 32 && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.k % 8 == 0 &&
-         p.k >= 8;
+         p.k >= 8 && 2 * (64 * p.ldb + p.k) < lim && 2 * (32 * p.lda + p.k) < lim;
 }
 
 bool skinny_fits(int t, int64_t m) { return m <= 16 * kSkinny[t].mb; }
 
-int skinny_choose(int64_t m, int64_t n) {
-  if (m > 16) return 1;
-  return (n / 32 >= 256) ? 0 : 2;
-}
+int skinny_choose(int64_t m, int64_t) { return m > 16 ? 1 : 4; }
 
 // Tile choice by shape class.  Large problems take the biggest tile the grid
 // can still fill the chip with; small and ragged ones take smaller tiles so
@@ -93,16 +97,16 @@ int choose_tile(int64_t m, int64_t n) {
 int choose_generic(int64_t m, int64_t n) { return cdiv(m, 128) * cdiv(n, 128) >= 256 ? 1 : 0; }
 
 struct Launch {
-  int bm, bn, bk, threads, stages, lds;
+  int bm, bn, bk, threads, stages, lds, dyn_lds;  // lds: total bytes; dyn_lds: dynamic part
 };
 
 Launch launch_shape(int variant, int tile) {
   if (variant == TG_VARIANT_SKINNY) {
     const tg::SkinnyShape& s = kSkinny[tile];
-    return Launch{16 * s.mb, 16 * s.nblk, 32 * s.unroll, 64 * s.waves, 1, tg::skinny_lds_of(s)};
+    return Launch{16 * s.mb, 16 * s.nb, s.sk, 64 * s.waves, s.stages, tg::skinny_lds_of(s), 0};
   }
   const TileShape& t = variant == TG_VARIANT_TILE ? kTiles[tile] : kGenericTiles[tile];
-  return Launch{t.bm, t.bn, t.bk, 64 * t.wm * t.wn, t.stages, tg::lds_bytes_of(t)};
+  return Launch{t.bm, t.bn, t.bk, 64 * t.wm * t.wn, t.stages, tg::lds_bytes_of(t), tg::lds_bytes_of(t)};
 }
 
 void fill_shape(gemm_plan_t* p) {
@@ -133,6 +137,15 @@ const char* tg_status_str(tg_status s) {
 }
 
 int32_t tg_abi_version(void) { return TG_ABI_VERSION; }
+
+int32_t tg_variant_tiles(int32_t variant) {
+  switch (variant) {
+    case TG_VARIANT_GENERIC: return kNumGeneric;
+    case TG_VARIANT_TILE: return kNumTiles;
+    case TG_VARIANT_SKINNY: return kNumSkinny;
+  }
+  return 0;
+}
 
 tg_status gemm_plan(gemm_plan_t* plan, tg_dtype in_type, tg_dtype out_type, int trans_a, int trans_b, int64_t m,
                     int64_t n, int64_t k, int64_t lda, int64_t ldb, int64_t ldc) {
@@ -244,11 +257,11 @@ static tg_status launch(const gemm_plan_t* plan, int64_t batch, int64_t sA, int6
   const int64_t groups = (int64_t)a.tiles_m * a.tiles_n;
   if (groups >= ((int64_t)1 << 31)) return TG_ERR_INVALID;
   const dim3 grid((unsigned)groups, (unsigned)(batch < 65535 ? batch : 65535));
-  if (l.lds > 64 * 1024) {
-    if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, l.lds) != hipSuccess)
+  if (l.dyn_lds > 64 * 1024) {
+    if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, l.dyn_lds) != hipSuccess)
       return TG_ERR_HIP;
   }
-  hipLaunchKernelGGL(fn, grid, dim3(l.threads), (size_t)l.lds, stream, a);
+  hipLaunchKernelGGL(fn, grid, dim3(l.threads), (size_t)l.dyn_lds, stream, a);
   return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 

@@ -45,18 +45,24 @@ constexpr int kNumGeneric = sizeof(kGenericTiles) / sizeof(kGenericTiles[0]);
 
 constexpr int lds_bytes_of(const TileShape& t) { return t.stages * (t.bm * t.bk + t.bk * t.bn) * 2; }
 
-// Skinny (M <= 32) streaming kernel: MB 16-row blocks, NBLK 16-column blocks
-// per work-group, WAVES waves splitting K, UNROLL 32-deep K blocks in flight.
+// Skinny (M <= 32) streaming kernel: MB 16-row blocks of A and C, NB 16-row
+// blocks of B (16*NB columns of C) per work-group, WAVES waves, STAGES LDS
+// stage buffers of SK k-elements.  LDS is static: STAGES * (16*NB + 16*MB)
+// rows * 2*SK bytes.
 struct SkinnyShape {
-  int mb, nblk, waves, unroll;
+  int mb, nb, waves, stages, sk;
 };
 constexpr SkinnyShape kSkinny[] = {
-    {1, 2, 8, 4},  // 0: M <= 16, 32 columns per work-group
-    {2, 2, 8, 4},  // 1: M <= 32
-    {1, 1, 8, 8},  // 2: M <= 16, 16 columns per work-group
-    {1, 4, 8, 2},  // 3: M <= 16, 64 columns per work-group
+    {1, 2, 8, 6, 256},  // 0: M <= 16, 32 columns per work-group, 144 KiB
+    {2, 2, 8, 4, 256},  // 1: M <= 32, 128 KiB
+    {1, 2, 4, 6, 256},  // 2: M <= 16, 4 waves
+    {1, 2, 4, 8, 128},  // 3: M <= 16, 8 shallower stages, 96 KiB
+    {1, 1, 4, 5, 256},  // 4: M <= 16, 16 columns, 80 KiB (two work-groups per CU)
+    {1, 4, 8, 4, 256},  // 5: M <= 16, 64 columns, 160 KiB
+    {1, 2, 8, 5, 256},  // 6: M <= 16, 5 stages, 120 KiB
+    {1, 2, 8, 4, 256},  // 7: M <= 16, 4 stages, 96 KiB
 };
 constexpr int kNumSkinny = sizeof(kSkinny) / sizeof(kSkinny[0]);
-constexpr int skinny_lds_of(const SkinnyShape& s) { return s.waves * s.mb * s.nblk * 64 * 16; }
+constexpr int skinny_lds_of(const SkinnyShape& s) { return s.stages * (16 * s.nb + 16 * s.mb) * 2 * s.sk; }
 
 }  // namespace tg

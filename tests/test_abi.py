@@ -59,6 +59,18 @@ def test_plan_struct_layout_matches_header(tmp_path):
         assert getattr(tg.GemmPlan, f).offset == off, f
 
 
+def test_variant_tile_counts():
+    counts = [tg.variant_tiles(v) for v in (tg.VARIANT_GENERIC, tg.VARIANT_TILE, tg.VARIANT_SKINNY)]
+    assert all(c >= 1 for c in counts)
+    assert tg.variant_tiles(7) == 0 and tg.variant_tiles(-1) == 0
+    # the last valid index of each variant passes the launcher's re-validation; one past it does not
+    st, p = raw_plan(m=64, n=64, k=64)
+    for v, c in zip((tg.VARIANT_GENERIC, tg.VARIANT_TILE), counts[:2]):
+        q = tg.GemmPlan.from_buffer_copy(p)
+        q.variant, q.tile = v, c
+        assert tg.lib().gemm_run(ctypes.byref(q), 16, 16, 16, None) == tg.TG_ERR_UNSUPPORTED
+
+
 def test_status_strings():
     assert tg.status_str(tg.TG_OK) == "ok"
     assert tg.status_str(tg.TG_ERR_INVALID) == "invalid argument"
