@@ -48,10 +48,16 @@ __device__ __forceinline__ void skinny_dma(__amdgpu_buffer_rsrc_t rs, uint32_t o
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (int)off, 0, 0, AUX);
 }
 
+// Wait until at most N of this wave's vector loads are outstanding and all of
+// its LDS reads have returned.  The LDS part matters: the buffer refilled
+// right after the next barrier is the one read in the step before it, and a
+// refill that reads out of range (past K) is answered with zeros at once,
+// without a trip to memory -- so every wave's reads of that buffer must be
+// complete before any wave may pass the barrier.
 template <int N>
 __device__ __forceinline__ void skinny_wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));  // lgkmcnt(0)
 }
 
 // A work-group barrier that orders memory operations for the compiler only;
@@ -194,8 +200,8 @@ __global__ void __launch_bounds__(WAVES * 64) skinny_gemm_kernel(GemmArgs args) 
 #pragma unroll
       for (int s = 0; s < S; ++s) {
         const int idx = r * S + s;
-        skinny_wait_vmcnt<(S - 2) * PW>();  // this wave's loads of stage idx landed
-        skinny_barrier();                   // ... and everyone's; buffer s-1 is free
+        skinny_wait_vmcnt<(S - 2) * PW>();  // own loads of stage idx landed, own reads done
+        skinny_barrier();                   // ... everyone's: buffer s-1 is free
         dma((s + S - 1) % S, idx + S - 1);
         compute(s);
       }

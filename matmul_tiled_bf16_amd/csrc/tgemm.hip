@@ -80,7 +80,7 @@ bool skinny_ok(const gemm_plan_t& p) {
 
 bool skinny_fits(int t, int64_t m) { return m <= 16 * kSkinny[t].mb; }
 
-int skinny_choose(int64_t m, int64_t) { return m > 16 ? 1 : 4; }
+int skinny_choose(int64_t m, int64_t) { return m > 16 ? 1 : 5; }
 
 // Tile choice by shape class.  Large problems take the biggest tile the grid
 // can still fill the chip with; small and ragged ones take smaller tiles so

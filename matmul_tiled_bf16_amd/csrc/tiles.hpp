@@ -55,12 +55,12 @@ struct SkinnyShape {
 constexpr SkinnyShape kSkinny[] = {
     {1, 2, 8, 6, 256},  // 0: M <= 16, 32 columns per work-group, 144 KiB
     {2, 2, 8, 4, 256},  // 1: M <= 32, 128 KiB
-    {1, 2, 4, 6, 256},  // 2: M <= 16, 4 waves
-    {1, 2, 4, 8, 128},  // 3: M <= 16, 8 shallower stages, 96 KiB
+    {1, 1, 8, 5, 256},  // 2: M <= 16, 16 columns, 8 waves, 80 KiB
+    {1, 1, 4, 5, 128},  // 3: M <= 16, 16 columns, 40 KiB (four work-groups per CU)
     {1, 1, 4, 5, 256},  // 4: M <= 16, 16 columns, 80 KiB (two work-groups per CU)
-    {1, 4, 8, 4, 256},  // 5: M <= 16, 64 columns, 160 KiB
-    {1, 2, 8, 5, 256},  // 6: M <= 16, 5 stages, 120 KiB
-    {1, 2, 8, 4, 256},  // 7: M <= 16, 4 stages, 96 KiB
+    {1, 1, 4, 4, 256},  // 5: M <= 16, 16 columns, 64 KiB
+    {1, 1, 4, 8, 128},  // 6: M <= 16, 16 columns, 8 shallow stages, 64 KiB
+    {1, 2, 8, 4, 256},  // 7: M <= 16, 32 columns, 96 KiB
 };
 constexpr int kNumSkinny = sizeof(kSkinny) / sizeof(kSkinny[0]);
 constexpr int skinny_lds_of(const SkinnyShape& s) { return s.stages * (16 * s.nb + 16 * s.mb) * 2 * s.sk; }

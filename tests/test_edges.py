@@ -139,7 +139,10 @@ def test_every_tile_gives_the_same_answer():
 def test_skinny_variants_and_tails():
     cases = [(t, 16) for t in range(tg.variant_tiles(tg.VARIANT_SKINNY)) if t != 1] + [(1, 32), (1, 17), (2, 5)]
     for tile, m in cases:
-        for n, k in [(8192, 1024), (100, 1000), (33, 8)]:
+        # K of only a few stages makes most ring refills read out of range
+        # (they return zeros at once): the refill must not overtake another
+        # wave's reads of the buffer it overwrites
+        for n, k in [(8192, 1024), (4096, 512), (100, 1000), (33, 8)]:
             got, ref, A, B, pl, _ = run_case(m, n, k, 0, 1, "bf16", seed=tile + n, variant=tg.VARIANT_SKINNY,
                                              tile=tile)
             check(got, ref, tol_fp32(k, oracle.max_abs(A), oracle.max_abs(B)), "bf16",
