@@ -114,9 +114,9 @@ def main():
 
     def step(i):
         pl = tg.plan(p.m, p.n, p.k, trans_a=p.trans_a, trans_b=p.trans_b, in_dtype=tin, out_dtype=tout,
-                     lda=p.lda, ldb=p.ldb, ldc=p.ldc)
+                     lda=p.lda, ldb=p.ldb, ldc=p.ldc, batch=p.batch)
         if args.tile is not None:
-            pl.tile = args.tile  # same variant; the launcher re-validates it
+            pl = tg.plan_tile(pl, pl.variant, args.tile)
         B = Bs[i % len(Bs)]
         C = Cs[i % len(Cs)]
         if p.batch == 1:
@@ -129,24 +129,19 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        starts[i].record(stream)
         pl = step(i)
-        ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    timed_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms_per_step = wall * 1e3 / args.steps
     assert torch.isfinite(Cs[0].float()).all().item(), "non-finite output"
 
-    # Kernel durations: the same launches, queued while the stream is held by a
-    # GPU-side sleep, so that host time between launches (plan, marshalling)
-    # cannot show up between the events.  For launches longer than the host's
-    # per-step time this equals the timed region's own per-launch events.
+    # Kernel durations, measured live with HIP events on the launch stream: the
+    # same launches, queued while the stream is held by a GPU-side sleep, so
+    # that host time between launches (plan, marshalling) cannot show up
+    # between the events.
     mean_ms, kms, queued_ahead = gated_kernel_ms(torch, stream, step, args.steps, max(args.warmup, 1))
     kernel_s = mean_ms / 1e3
 
@@ -185,7 +180,6 @@ def main():
                      "kernel_ms": round(kernel_s * 1e3, 5),
                      "kernel_ms_each_min": round(float(np.min(kms)), 5),
                      "kernel_ms_each_p90": round(float(np.percentile(kms, 90)), 5),
-                     "kernel_ms_timed_region": round(float(np.mean(timed_ms)), 5),
                      "launches_queued_ahead": bool(queued_ahead),
                      "algorithmic": {"flops": flops, "bytes": nbytes}},
     }

@@ -62,6 +62,7 @@ typedef enum {
 /* plan.flags bits */
 #define TG_FLAG_EVEN_K 0x1 /* K is a multiple of the K-tile: no masked K step */
 #define TG_FLAG_VEC16 0x2  /* leading dims and contiguous extents allow 16-byte loads */
+#define TG_FLAG_ROTATE_K 0x4 /* tile kernel: work-groups start their K walks at different steps */
 
 /*
  * A plan: caller-owned plain data, filled by gemm_plan(), read by gemm_run()
@@ -103,6 +104,27 @@ typedef struct {
  */
 tg_status gemm_plan(gemm_plan_t* plan, tg_dtype in_type, tg_dtype out_type, int trans_a, int trans_b,
                     int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb, int64_t ldc);
+
+/*
+ * bmm_plan -- gemm_plan for a batch of `batch` >= 1 products of the same
+ * shape (run with bmm_run): the tile choice counts work items over the whole
+ * batch.  gemm_plan(...) is bmm_plan(..., 1).  Same errors as gemm_plan, plus
+ * TG_ERR_INVALID for batch < 1.  Any valid plan may be passed to bmm_run with
+ * any batch count; this one is tuned for the count given here.
+ */
+tg_status bmm_plan(gemm_plan_t* plan, tg_dtype in_type, tg_dtype out_type, int trans_a, int trans_b,
+                   int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb, int64_t ldc, int64_t batch);
+
+/*
+ * gemm_plan_tile -- re-plan a valid plan for a caller-chosen kernel variant
+ * (tg_variant) and tile index (0 .. tg_variant_tiles(variant)-1): fills the
+ * same derived fields gemm_plan fills (bm, bn, bk, wg_threads, stages, flags,
+ * lds_bytes, tiles_m, tiles_n) for that choice.  Returns TG_ERR_INVALID for a
+ * null or stale plan and TG_ERR_UNSUPPORTED for a variant/tile that cannot
+ * run this problem; the plan is left unchanged on error.  Every choice gives
+ * the same result up to the order of fp32 additions.
+ */
+tg_status gemm_plan_tile(gemm_plan_t* plan, int32_t variant, int32_t tile);
 
 /*
  * gemm_run -- enqueue C = op(A) op(B) on `stream` (0 = the null stream) and

@@ -24,7 +24,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "tgemm.h")
 TG_BF16, TG_FP16, TG_FP32 = 0, 1, 2
 TG_OK, TG_ERR_INVALID, TG_ERR_UNSUPPORTED, TG_ERR_HIP = 0, 1, 2, 3
 VARIANT_GENERIC, VARIANT_TILE, VARIANT_SKINNY = 0, 1, 2
-FLAG_EVEN_K, FLAG_VEC16 = 0x1, 0x2
+FLAG_EVEN_K, FLAG_VEC16, FLAG_ROTATE_K = 0x1, 0x2, 0x4
 
 
 def _abi_version_from_header() -> int:
@@ -83,6 +83,11 @@ def lib() -> ctypes.CDLL:
         L.tg_abi_version.argtypes = []
         L.tg_variant_tiles.restype = i32
         L.tg_variant_tiles.argtypes = [i32]
+        L.bmm_plan.restype = ctypes.c_int
+        L.bmm_plan.argtypes = [ctypes.POINTER(GemmPlan), ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                               i64, i64, i64, i64, i64, i64, i64]
+        L.gemm_plan_tile.restype = ctypes.c_int
+        L.gemm_plan_tile.argtypes = [ctypes.POINTER(GemmPlan), i32, i32]
         if L.tg_abi_version() != _abi_version_from_header():
             raise RuntimeError("libtgemm.so was built from a different tgemm.h (ABI version mismatch)")
         _lib = L
@@ -111,8 +116,8 @@ def _dtype_code(dt) -> int:
 
 def plan(m: int, n: int, k: int, *, trans_a: bool = False, trans_b: bool = False, in_dtype=None,
          out_dtype=None, lda: Optional[int] = None, ldb: Optional[int] = None,
-         ldc: Optional[int] = None) -> GemmPlan:
-    """gemm_plan(): validate and choose kernel/tile (host only)."""
+         ldc: Optional[int] = None, batch: int = 1) -> GemmPlan:
+    """bmm_plan() (gemm_plan() for batch 1): validate and choose kernel/tile (host only)."""
     import torch
     in_dtype = torch.bfloat16 if in_dtype is None else in_dtype
     out_dtype = torch.float32 if out_dtype is None else out_dtype
@@ -120,11 +125,20 @@ def plan(m: int, n: int, k: int, *, trans_a: bool = False, trans_b: bool = False
     ldb = ldb if ldb is not None else max(1, k if trans_b else n)
     ldc = ldc if ldc is not None else max(1, n)
     p = GemmPlan()
-    st = lib().gemm_plan(ctypes.byref(p), _dtype_code(in_dtype), _dtype_code(out_dtype), int(trans_a),
-                         int(trans_b), m, n, k, lda, ldb, ldc)
+    st = lib().bmm_plan(ctypes.byref(p), _dtype_code(in_dtype), _dtype_code(out_dtype), int(trans_a),
+                        int(trans_b), m, n, k, lda, ldb, ldc, batch)
     if st != TG_OK:
-        raise TgError(st, "gemm_plan")
+        raise TgError(st, "bmm_plan")
     return p
+
+
+def plan_tile(p: GemmPlan, variant: int, tile: int) -> GemmPlan:
+    """gemm_plan_tile(): a copy of `p` re-planned for the given variant and tile."""
+    q = GemmPlan.from_buffer_copy(p)
+    st = lib().gemm_plan_tile(ctypes.byref(q), variant, tile)
+    if st != TG_OK:
+        raise TgError(st, "gemm_plan_tile")
+    return q
 
 
 def _stream_handle(stream) -> int:
@@ -202,6 +216,6 @@ def bmm(A, B, *, trans_a: bool = False, trans_b: bool = False, out_dtype=None, o
     if out is None:
         out = torch.empty((batch, m, n), dtype=out_dtype, device=A.device)
     p = plan(m, n, k, trans_a=trans_a, trans_b=trans_b, in_dtype=A.dtype, out_dtype=out_dtype, lda=_ld(A),
-             ldb=_ld(B), ldc=_ld(out))
+             ldb=_ld(B), ldc=_ld(out), batch=max(batch, 1))
     bmm_run(p, batch, A.stride(0), B.stride(0), out.stride(0), A, B, out, stream)
     return out

@@ -26,6 +26,7 @@ struct GemmArgs {
   int64_t sA, sB, sC;  // batch strides, elements
   int64_t batch;
   int32_t tiles_m, tiles_n;
+  int32_t rotate_k;  // nonzero: each work-group starts its walk over K at a different step
 };
 
 using KernelFn = void (*)(GemmArgs);
@@ -143,6 +144,31 @@ __device__ __forceinline__ void tile_coords(int32_t bid, int32_t tiles_m, int32_
   const int32_t first_m = bidx * GROUP_M;
   const int32_t gsz = min(tiles_m - first_m, GROUP_M);
   const int32_t in_band = id - bidx * band;
+  pm = first_m + in_band % gsz;
+  pn = in_band / gsz;
+}
+
+// Flat work index -> (matrix of the batch, tile row, tile column).  Work
+// item w0 is assumed to run on XCD w0 mod 8 (the dispatcher deals
+// consecutive work-groups round-robin over the XCDs, and a grid that loops
+// over work items strides by a multiple of 8).  Each XCD gets one contiguous
+// run of the (batch, tile) sequence, so a matrix's tiles -- which share that
+// matrix's A and B -- meet in one XCD's L2 instead of all eight; inside a
+// matrix, tiles go in bands of GROUP_M tile rows as in tile_coords.
+template <int GROUP_M>
+__device__ __forceinline__ void work_coords(int64_t w0, int64_t total, int32_t tiles_m, int32_t tiles_n,
+                                            int64_t& b, int32_t& pm, int32_t& pn) {
+  const int64_t per = total >> 3, rem = total & 7;
+  const int64_t x = w0 & 7, local = w0 >> 3;
+  const int64_t id = x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
+  const int64_t G = (int64_t)tiles_m * tiles_n;
+  b = id / G;
+  const int32_t t = (int32_t)(id - b * G);
+  const int32_t band = GROUP_M * tiles_n;
+  const int32_t bidx = t / band;
+  const int32_t first_m = bidx * GROUP_M;
+  const int32_t gsz = min(tiles_m - first_m, GROUP_M);
+  const int32_t in_band = t - bidx * band;
   pm = first_m + in_band % gsz;
   pn = in_band / gsz;
 }

@@ -69,15 +69,17 @@ __global__ void __launch_bounds__(WM * WN * 64) generic_gemm_kernel(GemmArgs arg
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
-  int32_t pm, pn;
-  tile_coords<8>(blockIdx.x, args.tiles_m, args.tiles_n, pm, pn);
-  const int64_t m0 = (int64_t)pm * BM, n0 = (int64_t)pn * BN;
   const int64_t M = args.M, N = args.N, K = args.K;
   const int64_t nk = (K + BK - 1) / BK;
 
   GA ga;
   GB gb;
-  for (int64_t b = blockIdx.y; b < args.batch; b += gridDim.y) {
+  const int64_t total = (int64_t)args.tiles_m * args.tiles_n * args.batch;
+  for (int64_t w0 = blockIdx.x; w0 < total; w0 += gridDim.x) {
+    int64_t b;
+    int32_t pm, pn;
+    work_coords<8>(w0, total, args.tiles_m, args.tiles_n, b, pm, pn);
+    const int64_t m0 = (int64_t)pm * BM, n0 = (int64_t)pn * BN;
     const uint16_t* Ab = args.A + b * args.sA;
     const uint16_t* Bb = args.B + b * args.sB;
     f32x16 acc[FM][FN];

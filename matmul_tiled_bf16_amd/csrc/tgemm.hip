@@ -80,21 +80,29 @@ bool skinny_ok(const gemm_plan_t& p) {
 
 bool skinny_fits(int t, int64_t m) { return m <= 16 * kSkinny[t].mb; }
 
-int skinny_choose(int64_t m, int64_t) { return m > 16 ? 1 : 5; }
+int skinny_choose(int64_t m, int64_t) { return m > 16 ? 1 : 0; }
 
-// Tile choice by shape class.  Large problems take the biggest tile the grid
-// can still fill the chip with; small and ragged ones take smaller tiles so
-// that there are at least ~256 work-groups ("Optimize Triton Block
-// Parameters": shape-specific tuning, a small M wants a small BLOCK_M).
-int choose_tile(int64_t m, int64_t n) {
-  auto tiles = [&](int t) { return cdiv(m, kTiles[t].bm) * cdiv(n, kTiles[t].bn); };
+// Tile choice by shape class and bound ("Optimize Triton Block Parameters",
+// Step 1 roofline classification and shape-specific tuning; a small M wants a
+// small BLOCK_M).  Work items are tiles times batch matrices.
+//  * MFMA-bound problems (arithmetic intensity above MI355X's ~312 FLOP/B
+//    ridge) take the 256x256 8-wave tile when there are >= 2 items per CU;
+//  * HBM-bound ones take 128x128 tiles, two work-groups per CU, whose
+//    operand panels and 1 KiB row-segment stores keep the streams long;
+//  * small and ragged problems take smaller tiles so that there are at least
+//    ~256 work-groups.
+int choose_tile(int64_t m, int64_t n, int64_t k, int64_t batch, int out_size) {
+  auto items = [&](int t) { return cdiv(m, kTiles[t].bm) * cdiv(n, kTiles[t].bn) * batch; };
   if (m <= 32) return 5;
-  if (tiles(8) >= 512) return 8;  // 256x256, 8 waves: >= 2 tiles per CU
-  if (tiles(1) >= 256) return 1;  // 128x128
-  return 0;                       // 64x64
+  const double flops = 2.0 * (double)m * (double)n * (double)k;
+  const double bytes = 2.0 * ((double)m * k + (double)k * n) + (double)out_size * m * n;
+  const bool mfma_bound = bytes > 0 && flops / bytes > 312.5;
+  if (mfma_bound && items(8) >= 512) return 8;  // 256x256, 8 waves
+  if (items(13) >= 256) return mfma_bound ? 1 : 13;  // 128x128
+  return 0;                                          // 64x64
 }
 
-int choose_generic(int64_t m, int64_t n) { return cdiv(m, 128) * cdiv(n, 128) >= 256 ? 1 : 0; }
+int choose_generic(int64_t m, int64_t n, int64_t batch) { return cdiv(m, 128) * cdiv(n, 128) * batch >= 256 ? 1 : 0; }
 
 struct Launch {
   int bm, bn, bk, threads, stages, lds, dyn_lds;  // lds: total bytes; dyn_lds: dynamic part
@@ -120,6 +128,11 @@ void fill_shape(gemm_plan_t* p) {
   p->tiles_m = p->variant == TG_VARIANT_SKINNY ? 1 : cdiv(p->m, p->bm);
   p->tiles_n = cdiv(p->n, p->bn);
   p->flags = (p->flags & ~TG_FLAG_EVEN_K) | ((p->bk > 0 && p->k % p->bk == 0) ? TG_FLAG_EVEN_K : 0);
+  // Rotated K walks when no two tiles share an operand panel in the same
+  // step (a single row or column of tiles): each work-group streams a panel
+  // of its own, and lock-step walks would crowd the same HBM channels.
+  const bool rotate = p->variant == TG_VARIANT_TILE && (p->tiles_m == 1 || p->tiles_n == 1);
+  p->flags = (p->flags & ~TG_FLAG_ROTATE_K) | (rotate ? TG_FLAG_ROTATE_K : 0);
 }
 
 }  // namespace
@@ -147,9 +160,15 @@ int32_t tg_variant_tiles(int32_t variant) {
   return 0;
 }
 
-tg_status gemm_plan(gemm_plan_t* plan, tg_dtype in_type, tg_dtype out_type, int trans_a, int trans_b, int64_t m,
-                    int64_t n, int64_t k, int64_t lda, int64_t ldb, int64_t ldc) {
+tg_status bmm_plan(gemm_plan_t* plan, tg_dtype in_type, tg_dtype out_type, int trans_a, int trans_b, int64_t m,
+                   int64_t n, int64_t k, int64_t lda, int64_t ldb, int64_t ldc, int64_t batch) {
   if (!plan) return TG_ERR_INVALID;
+  if (batch < 1) {
+    gemm_plan_t p = {};
+    p.abi_version = -1;
+    *plan = p;
+    return TG_ERR_INVALID;
+  }
   gemm_plan_t p = {};
   p.abi_version = -1;
   *plan = p;
@@ -184,14 +203,39 @@ tg_status gemm_plan(gemm_plan_t* plan, tg_dtype in_type, tg_dtype out_type, int 
     p.tile = skinny_choose(m, n);
   } else if (p.flags & TG_FLAG_VEC16) {
     p.variant = TG_VARIANT_TILE;
-    p.tile = choose_tile(m, n);
+    p.tile = choose_tile(m, n, k, batch, out_type == TG_FP32 ? 4 : 2);
   } else {
     p.variant = TG_VARIANT_GENERIC;
-    p.tile = choose_generic(m, n);
+    p.tile = choose_generic(m, n, batch);
   }
   fill_shape(&p);
   if (p.tiles_m * p.tiles_n >= lim) return TG_ERR_INVALID;
   p.abi_version = TG_ABI_VERSION;
+  *plan = p;
+  return TG_OK;
+}
+
+tg_status gemm_plan(gemm_plan_t* plan, tg_dtype in_type, tg_dtype out_type, int trans_a, int trans_b, int64_t m,
+                    int64_t n, int64_t k, int64_t lda, int64_t ldb, int64_t ldc) {
+  return bmm_plan(plan, in_type, out_type, trans_a, trans_b, m, n, k, lda, ldb, ldc, 1);
+}
+
+tg_status gemm_plan_tile(gemm_plan_t* plan, int32_t variant, int32_t tile) {
+  if (!plan || plan->abi_version != TG_ABI_VERSION) return TG_ERR_INVALID;
+  gemm_plan_t p = *plan;
+  if (variant == TG_VARIANT_SKINNY) {
+    if (tile < 0 || tile >= kNumSkinny || !skinny_ok(p) || !skinny_fits(tile, p.m)) return TG_ERR_UNSUPPORTED;
+  } else if (variant == TG_VARIANT_TILE) {
+    if (tile < 0 || tile >= kNumTiles || !vec_ok(p)) return TG_ERR_UNSUPPORTED;
+  } else if (variant == TG_VARIANT_GENERIC) {
+    if (tile < 0 || tile >= kNumGeneric) return TG_ERR_UNSUPPORTED;
+  } else {
+    return TG_ERR_UNSUPPORTED;
+  }
+  p.variant = variant;
+  p.tile = tile;
+  fill_shape(&p);
+  if (p.tiles_m * p.tiles_n >= ((int64_t)1 << 31)) return TG_ERR_UNSUPPORTED;
   *plan = p;
   return TG_OK;
 }
@@ -223,7 +267,7 @@ static tg_status launch(const gemm_plan_t* plan, int64_t batch, int64_t sA, int6
                        (batch == 1 || (sA % 8 == 0 && sB % 8 == 0 && sC % 8 == 0));
   if (variant != TG_VARIANT_GENERIC && !aligned) {
     variant = TG_VARIANT_GENERIC;
-    tile = choose_generic(p.m, p.n);
+    tile = choose_generic(p.m, p.n, batch);
   }
 
   tg::GemmArgs a;
@@ -240,6 +284,7 @@ static tg_status launch(const gemm_plan_t* plan, int64_t batch, int64_t sA, int6
   a.sB = sB;
   a.sC = sC;
   a.batch = batch;
+  a.rotate_k = (variant == TG_VARIANT_TILE && (p.flags & TG_FLAG_ROTATE_K)) ? 1 : 0;
 
   const Launch l = launch_shape(variant, tile);
   const int io = p.in_type == TG_BF16 ? 0 : 1, oo = p.out_type == TG_FP32 ? 0 : 1;
@@ -256,7 +301,16 @@ static tg_status launch(const gemm_plan_t* plan, int64_t batch, int64_t sA, int6
   }
   const int64_t groups = (int64_t)a.tiles_m * a.tiles_n;
   if (groups >= ((int64_t)1 << 31)) return TG_ERR_INVALID;
-  const dim3 grid((unsigned)groups, (unsigned)(batch < 65535 ? batch : 65535));
+  dim3 grid;
+  if (variant == TG_VARIANT_SKINNY) {
+    grid = dim3((unsigned)groups, (unsigned)(batch < 65535 ? batch : 65535));
+  } else {
+    // one work-group per (matrix, tile) work item, flattened; beyond 2^30
+    // items each work-group loops (the stride stays a multiple of 8, which
+    // keeps every item on the XCD the kernel's tile order assumes)
+    const int64_t total = groups * batch, cap = (int64_t)1 << 30;
+    grid = dim3((unsigned)(total < cap ? total : cap), 1);
+  }
   if (l.dyn_lds > 64 * 1024) {
     if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, l.dyn_lds) != hipSuccess)
       return TG_ERR_HIP;

@@ -202,6 +202,83 @@ __device__ __forceinline__ void store_tile_vec(const void* Ctile, int64_t bytes,
   }
 }
 
+// LDS-staged store of the work-group's BM x BN tile ("Triton Optimization
+// Reference", section 5: the epilogue goes out in subtiles through shared
+// memory).  The MFMA result layout gives each lane four consecutive columns
+// of one row, so direct stores write 32 rows x 32 bytes per instruction --
+// a scattered pattern the memory system handles poorly.  Here the waves
+// first write their blocks (already converted to Out) into LDS, then every
+// thread reads 16 consecutive bytes of a row and stores them, so one store
+// instruction covers 1 KiB of whole row segments of C.  LDS rows are split
+// into 16-byte units and unit u of row r sits at position u ^ (r & SM), which
+// keeps the writes of 16 rows on distinct banks; the readers undo the XOR
+// when they form the global column.  When the tile does not fit the LDS the
+// kernel owns, it goes in PASSES row bands, one row of waves per band.
+// Rows past M are dropped by the descriptor's size; 16-byte units at or past
+// column N get an out-of-range offset (the caller guarantees N is a multiple
+// of 16 / sizeof(Out)).
+template <typename Out, int BM, int BN, int WM, int WN, int FM, int FN, int PASSES, int AUX>
+__device__ __forceinline__ void store_tile_lds(TG_LDS char* lds, void* Ctile, int64_t bytes, int64_t ldc,
+                                               int64_t n_left, int wave, int lane, const f32x16 (&acc)[FM][FN]) {
+  constexpr int NT = WM * WN * 64;
+  constexpr uint32_t es = sizeof(Out);
+  constexpr uint32_t ROWB = BN * es;          // bytes of one tile row
+  constexpr int UPR = ROWB / 16;              // 16-byte units per row
+  constexpr int SM = (UPR < 16 ? UPR : 16) - 1;
+  constexpr int RP = BM / PASSES;             // rows per band
+  constexpr int UNITS = RP * UPR;             // units per band
+  static_assert(UPR >= 4 && UNITS % NT == 0 && RP % (BM / WM) == 0, "epilogue band shape");
+  const __amdgpu_buffer_rsrc_t rs = store_rsrc(Ctile, bytes);
+  const int li = lane & 31, lg = lane >> 5;
+  const int wr = wave / WN, wn0 = (wave % WN) * (BN / WN);
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+    // waves whose rows fall in this band write them, converted, into LDS
+    if (wr * (BM / WM) / RP == pass) {
+      const int rbase = wr * (BM / WM) - pass * RP;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = rbase + i * 32 + li;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = wn0 + j * 32 + 8 * g + 4 * lg;  // 4 consecutive columns
+            const uint32_t byte = (uint32_t)col * es;
+            const uint32_t pos = (uint32_t)r * ROWB + ((((byte >> 4) ^ (uint32_t)(r & SM))) << 4) + (byte & 15);
+            const f32x16& a = acc[i][j];
+            if constexpr (es == 4) {
+              *(TG_LDS u32x4*)(lds + pos) =
+                  __builtin_bit_cast(u32x4, f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]});
+            } else {
+              *(TG_LDS u32x2*)(lds + pos) =
+                  u32x2{pack2<Out>(a[4 * g], a[4 * g + 1]), pack2<Out>(a[4 * g + 2], a[4 * g + 3])};
+            }
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+    block_barrier();
+    // every thread stores whole 16-byte units of rows, 1 KiB per instruction
+#pragma unroll
+    for (int k = 0; k < UNITS / NT; ++k) {
+      const int idx = k * NT + wave * 64 + lane;
+      const int r = idx / UPR, p = idx % UPR;
+      const u32x4 v = *(const TG_LDS u32x4*)(lds + (uint32_t)r * ROWB + (uint32_t)p * 16);
+      const int u = p ^ (r & SM);
+      const int col = u * (16 / es);
+      const uint32_t off =
+          col < n_left ? (uint32_t)((pass * RP + r) * ldc) * es + (uint32_t)col * es : kOutOfRange;
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, AUX);
+    }
+    if (pass + 1 < PASSES) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // this band's LDS reads are done before the next band's writes
+      block_barrier();
+    }
+  }
+}
+
 // Fragments of one 16-deep K slice for a wave's FM x FN blocks.
 template <int FM, int FN>
 struct Frags {
@@ -235,6 +312,13 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
   //    barrier must first retire this wave's reads of stage kt.
   constexpr bool EARLY = STAGES >= 3;
   constexpr int D = EARLY ? STAGES - 1 : STAGES;
+  // LDS-staged epilogue: in one band if the tile fits the ring's LDS, else in
+  // one band per row of waves; 0 = direct vector stores
+  constexpr uint32_t C_BYTES = (uint32_t)BM * BN * sizeof(Out), RING_BYTES = STAGES * STAGE;
+  constexpr int EPI_UPR = BN * (int)sizeof(Out) / 16;
+  constexpr int EPI_P = C_BYTES <= RING_BYTES ? 1 : (C_BYTES / WM <= RING_BYTES ? WM : 0);
+  constexpr int EPI_PASSES =
+      (EPI_P > 0 && EPI_UPR >= 4 && ((BM / (EPI_P ? EPI_P : 1)) * EPI_UPR) % (NW * 64) == 0) ? EPI_P : 0;
 
   extern __shared__ __attribute__((aligned(1024))) char tg_smem[];
   TG_LDS char* lds = (TG_LDS char*)tg_smem;
@@ -246,9 +330,6 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
   const int li = lane & 31, lg = lane >> 5;
   const int trh = lane >> 4, trs = lane & 15;
 
-  int32_t pm, pn;
-  tile_coords<8>(blockIdx.x, args.tiles_m, args.tiles_n, pm, pn);
-  const int64_t m0 = (int64_t)pm * BM, n0 = (int64_t)pn * BN;
   const int64_t M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
 
   const int dwave = wave - (NW - DW);  // index among the copy waves (< 0: computes only)
@@ -289,13 +370,42 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
   const int64_t a_step = A_KC ? (int64_t)BK * 2 : (int64_t)BK * lda * 2;
   const int64_t b_step = B_KC ? (int64_t)BK * 2 : (int64_t)BK * ldb * 2;
 
-  for (int64_t b = blockIdx.y; b < args.batch; b += gridDim.y) {
-    // running source pointers / remaining bytes of the next step to load
-    const char* a_ptr = (const char*)(args.A + b * args.sA + (A_KC ? m0 * lda : m0));
-    const char* b_ptr = (const char*)(args.B + b * args.sB + (B_KC ? n0 * ldb : n0));
-    int64_t a_left = A_KC ? ((M - 1 - m0) * lda + K) * 2 : ((K - 1) * lda + (M - m0)) * 2;
-    int64_t b_left = B_KC ? ((N - 1 - n0) * ldb + K) * 2 : ((K - 1) * ldb + (N - n0)) * 2;
-    int64_t k_left = K;  // K - k0 of the next step to load
+  // Walk order over the K steps.  Normally 0, 1, ...; with rotate_k the
+  // full steps are walked from a per-work-group starting step (the partial
+  // step, if any, stays last).  Work-groups otherwise run in lock-step and,
+  // when each streams an operand panel of its own, all of them hit the same
+  // offsets -- and HBM channels -- at the same time.  Tiles that share
+  // panels (grouped launch order) keep the plain order so that neighbours
+  // still meet in L2.
+  const int64_t total = (int64_t)args.tiles_m * args.tiles_n * args.batch;
+  for (int64_t w0 = blockIdx.x; w0 < total; w0 += gridDim.x) {
+    int64_t b;
+    int32_t pm, pn;
+    work_coords<8>(w0, total, args.tiles_m, args.tiles_n, b, pm, pn);
+    const int64_t m0 = (int64_t)pm * BM, n0 = (int64_t)pn * BN;
+    const int64_t rot = (args.rotate_k && nfull > 1) ? w0 % nfull : 0;
+    // source pointers / remaining bytes / K - k0 of the next step to load
+    const char* const a_base = (const char*)(args.A + b * args.sA + (A_KC ? m0 * lda : m0));
+    const char* const b_base = (const char*)(args.B + b * args.sB + (B_KC ? n0 * ldb : n0));
+    const int64_t a_left0 = A_KC ? ((M - 1 - m0) * lda + K) * 2 : ((K - 1) * lda + (M - m0)) * 2;
+    const int64_t b_left0 = B_KC ? ((N - 1 - n0) * ldb + K) * 2 : ((K - 1) * ldb + (N - n0)) * 2;
+    const char* a_ptr;
+    const char* b_ptr;
+    int64_t a_left, b_left, k_left;
+    int64_t ld_step = 0;  // walk position of the next step to load
+    auto seek = [&]() {
+      int64_t p = ld_step;
+      if (ld_step < nfull) {
+        p += rot;
+        p = p >= nfull ? p - nfull : p;
+      }
+      a_ptr = a_base + p * a_step;
+      a_left = a_left0 - p * a_step;
+      b_ptr = b_base + p * b_step;
+      b_left = b_left0 - p * b_step;
+      k_left = K - p * BK;
+    };
+    seek();
 
     auto issue = [&](uint32_t buf, auto full) {
       const uint32_t st = lds0 + buf * STAGE;
@@ -307,11 +417,8 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
         oa.template issue<true>((const uint16_t*)a_ptr, a_left, st, dwave, k_left);
         ob.template issue<true>((const uint16_t*)b_ptr, b_left, st + A_BYTES, dwave, k_left);
       }
-      a_ptr += a_step;
-      a_left -= a_step;
-      b_ptr += b_step;
-      b_left -= b_step;
-      k_left -= BK;
+      ++ld_step;
+      seek();
     };
 
     // LDS -> registers: read r (0 <= r < READS) of slice ks of the stage at
@@ -426,11 +533,8 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
             slice(cur, &nxt, ((buf + 1) % STAGES) * STAGE, 0, &rsa, &rsb, lds0 + dst, 0, PER_STEP);
           }
         }
-        a_ptr += a_step;
-        a_left -= a_step;
-        b_ptr += b_step;
-        b_left -= b_step;
-        k_left -= BK;
+        ++ld_step;
+        seek();
       };
       auto stage_dyn = [&](int64_t kt) {
         const uint32_t buf = (uint32_t)(kt % STAGES);
@@ -466,6 +570,17 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
     {
       const int64_t r0 = m0 + wm0, c0 = n0 + wn0;
       char* Cb = (char*)args.C + b * args.sC * (int64_t)sizeof(Out);
+      if constexpr (EPI_PASSES > 0) {
+        if (N % (16 / (int)sizeof(Out)) == 0) {  // uniform over the work-group
+          // every wave's reads of the last stage are done before LDS is reused
+          __builtin_amdgcn_s_waitcnt(0xC07F);
+          block_barrier();
+          store_tile_lds<Out, BM, BN, WM, WN, FM, FN, EPI_PASSES, 0>(
+              lds, Cb + (m0 * args.ldc + n0) * (int64_t)sizeof(Out),
+              ((M - 1 - m0) * args.ldc + (N - n0)) * (int64_t)sizeof(Out), args.ldc, N - n0, wave, lane, acc);
+          goto stored;
+        }
+      }
       if (N % 4 == 0 || n0 + BN <= N) {
         if (r0 < M && c0 < N)
           store_tile_vec<Out, FM, FN>(Cb + (r0 * args.ldc + c0) * (int64_t)sizeof(Out),
@@ -474,9 +589,10 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
       } else {
         store_tile<Out, FM, FN>(Cb, args.ldc, M, N, r0, c0, lane, acc);
       }
+    stored:;
     }
-    if (b + gridDim.y < args.batch) {
-      // the next matrix's prologue overwrites buffers other waves may still read
+    if (w0 + gridDim.x < total) {
+      // the next tile's prologue overwrites buffers other waves may still read
       wait_vmcnt<0>();
       block_barrier();
     }

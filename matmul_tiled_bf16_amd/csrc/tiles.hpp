@@ -34,6 +34,12 @@ constexpr TileShape kTiles[] = {
     // 8 waves, copies issued by the second wave of each SIMD only
     {256, 256, 64, 2, 4, 2, 1, 4},  // 14
     {256, 256, 32, 2, 4, 4, 1, 4},  // 15
+    // three or four work-groups per CU: small rings for short K, where the
+    // loads are latency-bound and only concurrency hides them
+    {128, 128, 32, 2, 2, 2, 4},  // 16: 32 KiB
+    {128, 128, 32, 2, 2, 3, 3},  // 17: 48 KiB
+    {64, 128, 64, 2, 2, 2, 3},   // 18: 32x64 per wave, 48 KiB
+    {128, 64, 64, 2, 2, 2, 4},   // 19: 64x32 per wave, 32 KiB
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -53,13 +59,13 @@ struct SkinnyShape {
   int mb, nb, waves, stages, sk;
 };
 constexpr SkinnyShape kSkinny[] = {
-    {1, 2, 8, 6, 256},  // 0: M <= 16, 32 columns per work-group, 144 KiB
+    {1, 1, 4, 3, 256},  // 0: M <= 16, 16 columns, 48 KiB (three work-groups per CU)
     {2, 2, 8, 4, 256},  // 1: M <= 32, 128 KiB
-    {1, 1, 8, 5, 256},  // 2: M <= 16, 16 columns, 8 waves, 80 KiB
-    {1, 1, 4, 5, 128},  // 3: M <= 16, 16 columns, 40 KiB (four work-groups per CU)
+    {1, 1, 2, 4, 256},  // 2: M <= 16, 16 columns, 2 waves, 64 KiB
+    {1, 1, 8, 4, 256},  // 3: M <= 16, 16 columns, 8 waves, 64 KiB
     {1, 1, 4, 5, 256},  // 4: M <= 16, 16 columns, 80 KiB (two work-groups per CU)
     {1, 1, 4, 4, 256},  // 5: M <= 16, 16 columns, 64 KiB
-    {1, 1, 4, 8, 128},  // 6: M <= 16, 16 columns, 8 shallow stages, 64 KiB
+    {2, 1, 4, 3, 256},  // 6: M <= 32, 16 columns, 72 KiB
     {1, 2, 8, 4, 256},  // 7: M <= 16, 32 columns, 96 KiB
 };
 constexpr int kNumSkinny = sizeof(kSkinny) / sizeof(kSkinny[0]);

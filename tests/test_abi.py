@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert {"gemm_plan", "gemm_run", "bmm_run", "tg_status_str", "tg_abi_version"} <= set(names)
+    assert {"gemm_plan", "bmm_plan", "gemm_plan_tile", "gemm_run", "bmm_run", "tg_status_str", "tg_abi_version",
+            "tg_variant_tiles"} <= set(names)
     L = tg.lib()
     for n in names:
         assert hasattr(L, n), f"libtgemm.so does not export {n}"
@@ -69,6 +70,26 @@ def test_variant_tile_counts():
         q = tg.GemmPlan.from_buffer_copy(p)
         q.variant, q.tile = v, c
         assert tg.lib().gemm_run(ctypes.byref(q), 16, 16, 16, None) == tg.TG_ERR_UNSUPPORTED
+
+
+def test_plan_tile_rederives_the_plan():
+    st, p = raw_plan(m=2048, n=128, k=2048)
+    assert st == tg.TG_OK
+    q = tg.plan_tile(p, tg.VARIANT_TILE, 1)          # 128 x 128: one column of tiles
+    assert (q.variant, q.tile, q.bm, q.bn, q.tiles_m, q.tiles_n) == (tg.VARIANT_TILE, 1, 128, 128, 16, 1)
+    assert q.flags & tg.FLAG_ROTATE_K and q.flags & tg.FLAG_EVEN_K
+    assert q.lds_bytes == roofline.lds_budget(128, 128, q.bk, q.stages)
+    r = tg.plan_tile(q, tg.VARIANT_GENERIC, 0)
+    assert r.variant == tg.VARIANT_GENERIC and not r.flags & tg.FLAG_ROTATE_K
+    L = tg.lib()
+    bad = tg.GemmPlan.from_buffer_copy(p)
+    for variant, tile in [(tg.VARIANT_TILE, tg.variant_tiles(tg.VARIANT_TILE)), (tg.VARIANT_SKINNY, 0), (9, 0)]:
+        assert L.gemm_plan_tile(ctypes.byref(bad), variant, tile) == tg.TG_ERR_UNSUPPORTED
+        assert bytes(bad) == bytes(p), "a failed re-plan leaves the plan unchanged"
+    stale = tg.GemmPlan.from_buffer_copy(p)
+    stale.abi_version = 0
+    assert L.gemm_plan_tile(ctypes.byref(stale), tg.VARIANT_TILE, 0) == tg.TG_ERR_INVALID
+    assert L.gemm_plan_tile(None, tg.VARIANT_TILE, 0) == tg.TG_ERR_INVALID
 
 
 def test_status_strings():
@@ -140,6 +161,14 @@ def test_plan_choices_for_the_workloads():
     assert p.variant == tg.VARIANT_TILE and p.flags & tg.FLAG_EVEN_K
     p = tg.plan(2048, 128, 2048)
     assert p.variant == tg.VARIANT_TILE
+    # batched attention shapes, planned for their batch of 128: 128x128 tiles (HBM-bound), and the
+    # single-column O = P V rotates its K walks
+    for mm, nn, kk, tb in [(2048, 2048, 128, True), (2048, 128, 2048, False)]:
+        p = tg.plan(mm, nn, kk, trans_b=tb, batch=128)
+        assert (p.variant, p.bm, p.bn) == (tg.VARIANT_TILE, 128, 128)
+        assert bool(p.flags & tg.FLAG_ROTATE_K) == (nn == 128)
+    with pytest.raises(tg.TgError):
+        tg.plan(64, 64, 64, batch=0)
     p = tg.plan(8192, 8192, 8192, out_dtype=torch.bfloat16)
     assert (p.variant, p.bm, p.bn, p.wg_threads) == (tg.VARIANT_TILE, 256, 256, 512) and p.tiles_m * p.tiles_n == 1024
     assert p.workspace_bytes == 0

@@ -52,7 +52,7 @@ def run_case(m, n, k, ta, tb, out_dtype="fp32", pad=(0, 0, 0), seed=0, dist=("no
     Cbuf = torch.full((rows_c * ldc + 64 + offset_elems,), CANARY, dtype=tout, device="cuda")
     pl = tg.plan(m, n, k, trans_a=ta, trans_b=tb, in_dtype=tin, out_dtype=tout, lda=lda, ldb=ldb, ldc=ldc)
     if variant is not None:
-        pl.variant, pl.tile = variant, tile
+        pl = tg.plan_tile(pl, variant, tile)
     st = tg.lib().gemm_run(ctypes.byref(pl), Ag.data_ptr() + 2 * offset_elems, Bg.data_ptr() + 2 * offset_elems,
                            Cbuf.data_ptr() + Cbuf.element_size() * offset_elems,
                            torch.cuda.current_stream().cuda_stream)
