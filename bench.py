@@ -67,6 +67,7 @@ def main():
                          "default 4 for HBM-bound workloads, 1 otherwise")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile", type=int, default=None, help="override the planner's tile (same variant)")
+    ap.add_argument("--no-persist", action="store_true", help="clear the plan's persistent-launch flag")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to calibrate FETCH_SIZE/WRITE_SIZE)")
@@ -117,6 +118,8 @@ def main():
                      lda=p.lda, ldb=p.ldb, ldc=p.ldc, batch=p.batch)
         if args.tile is not None:
             pl = tg.plan_tile(pl, pl.variant, args.tile)
+        if args.no_persist:
+            pl.flags &= ~tg.FLAG_PERSIST
         B = Bs[i % len(Bs)]
         C = Cs[i % len(Cs)]
         if p.batch == 1:
@@ -170,7 +173,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": p.name, "m": p.m, "n": p.n, "k": p.k, "batch": p.batch, "op": trans,
                    "in_dtype": p.in_dtype, "out_dtype": p.out_dtype, "b_copies": len(Bs),
-                   "variant": int(pl.variant), "tile_index": int(pl.tile)},
+                   "variant": int(pl.variant), "tile_index": int(pl.tile), "plan_flags": int(pl.flags)},
         "tflops": round(tflops, 2),
         "pct_mfma_peak": round(100 * flops / (ms_per_step / 1e3) / PEAK_MFMA, 2),
         "gbps": round(gbps, 1),

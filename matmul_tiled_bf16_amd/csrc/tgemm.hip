@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include <array>
+#include <atomic>
 
 #include "../../include/tgemm.h"
 #include "common.hpp"
@@ -133,6 +134,16 @@ void fill_shape(gemm_plan_t* p) {
   // of its own, and lock-step walks would crowd the same HBM channels.
   const bool rotate = p->variant == TG_VARIANT_TILE && (p->tiles_m == 1 || p->tiles_n == 1);
   p->flags = (p->flags & ~TG_FLAG_ROTATE_K) | (rotate ? TG_FLAG_ROTATE_K : 0);
+  // Persistent launches store straight from registers, 4 columns at a time.
+  // They pay off where the MFMA work per tile dwarfs its memory traffic (no
+  // work-group launch gap, the next tile's first copies overlap this tile's
+  // stores); HBM-bound shapes keep one work-group per tile and the LDS-staged
+  // row-segment stores, which measured faster for them.
+  const double flops = 2.0 * (double)p->m * (double)p->n * (double)p->k;
+  const double bytes = 2.0 * ((double)p->m * p->k + (double)p->k * p->n) +
+                       (p->out_type == TG_FP32 ? 4.0 : 2.0) * (double)p->m * p->n;
+  const bool persist = p->variant == TG_VARIANT_TILE && p->n % 4 == 0 && bytes > 0 && flops / bytes > 312.5;
+  p->flags = (p->flags & ~TG_FLAG_PERSIST) | (persist ? TG_FLAG_PERSIST : 0);
 }
 
 }  // namespace
@@ -240,6 +251,22 @@ tg_status gemm_plan_tile(gemm_plan_t* plan, int32_t variant, int32_t tile) {
   return TG_OK;
 }
 
+// Compute units of the current device, cached per device (the value never
+// changes; racing first calls store the same number).
+static int compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 static tg_status launch(const gemm_plan_t* plan, int64_t batch, int64_t sA, int64_t sB, int64_t sC, const void* A,
                         const void* B, void* C, hipStream_t stream) {
   if (!plan || plan->abi_version != TG_ABI_VERSION) return TG_ERR_INVALID;
@@ -285,6 +312,7 @@ static tg_status launch(const gemm_plan_t* plan, int64_t batch, int64_t sA, int6
   a.sC = sC;
   a.batch = batch;
   a.rotate_k = (variant == TG_VARIANT_TILE && (p.flags & TG_FLAG_ROTATE_K)) ? 1 : 0;
+  a.persist = 0;
 
   const Launch l = launch_shape(variant, tile);
   const int io = p.in_type == TG_BF16 ? 0 : 1, oo = p.out_type == TG_FP32 ? 0 : 1;
@@ -308,7 +336,16 @@ static tg_status launch(const gemm_plan_t* plan, int64_t batch, int64_t sA, int6
     // one work-group per (matrix, tile) work item, flattened; beyond 2^30
     // items each work-group loops (the stride stays a multiple of 8, which
     // keeps every item on the XCD the kernel's tile order assumes)
-    const int64_t total = groups * batch, cap = (int64_t)1 << 30;
+    const int64_t total = groups * batch;
+    int64_t cap = (int64_t)1 << 30;
+    if (variant == TG_VARIANT_TILE && (p.flags & TG_FLAG_PERSIST) && p.n % 4 == 0 && tg::persist_ok(kTiles[tile])) {
+      // persistent: one work-group per resident slot (a multiple of 8)
+      const int64_t slots = (int64_t)compute_units() * kTiles[tile].occ;
+      if (slots > 0 && total >= 2 * slots) {
+        cap = slots;
+        a.persist = 1;
+      }
+    }
     grid = dim3((unsigned)(total < cap ? total : cap), 1);
   }
   if (l.dyn_lds > 64 * 1024) {

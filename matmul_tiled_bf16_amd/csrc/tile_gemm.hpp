@@ -83,6 +83,31 @@ __device__ __forceinline__ void wait_steps(int64_t steps) {
   else wait_vmcnt<0, LGKM0>();
 }
 
+// As wait_steps, but EXTRA more operations (stores issued after the copies)
+// may stay outstanding.
+template <int PER_STEP, int EXTRA, int MAXSTEPS>
+__device__ __forceinline__ void wait_steps_plus(int64_t steps) {
+  // more than two steps are waited for as two (stricter, hence safe)
+  static_assert(MAXSTEPS >= 0 && MAXSTEPS <= 2, "0 .. 2 steps");
+  asm volatile("" ::: "memory");
+  if constexpr (MAXSTEPS >= 2) {
+    if (steps >= 2) {
+      wait_vmcnt<2 * PER_STEP + EXTRA, true>();
+      asm volatile("" ::: "memory");
+      return;
+    }
+  }
+  if constexpr (MAXSTEPS >= 1) {
+    if (steps >= 1) {
+      wait_vmcnt<PER_STEP + EXTRA, true>();
+      asm volatile("" ::: "memory");
+      return;
+    }
+  }
+  wait_vmcnt<EXTRA, true>();
+  asm volatile("" ::: "memory");
+}
+
 // Work-group barrier that orders memory operations only at compile time; the
 // caller has already waited for whatever the other waves must see.
 __device__ __forceinline__ void block_barrier() {
@@ -378,34 +403,54 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
   // panels (grouped launch order) keep the plain order so that neighbours
   // still meet in L2.
   const int64_t total = (int64_t)args.tiles_m * args.tiles_n * args.batch;
-  for (int64_t w0 = blockIdx.x; w0 < total; w0 += gridDim.x) {
-    int64_t b;
+  // Persistent mode (args.persist): a work-group walks several items and,
+  // once an item's K loop is done, issues the next item's prologue copies
+  // before this item's stores, so the next K loop starts while the stores
+  // drain.  Loads and stores retire through one in-order counter, so the
+  // first wait of a prefetched item lets exactly ST later operations -- the
+  // stores, a fixed count per wave -- stay outstanding.
+  constexpr int ST = FM * FN * 4;  // store instructions of store_tile_vec
+  constexpr bool PERSIST_OK = (D - 1) * PER_STEP + ST < 64;  // fits the counter
+  const bool persist = PERSIST_OK && args.persist != 0;
+  // the item being computed: matrix, tile origin, walk rotation, and the
+  // source pointers / remaining bytes / K - k0 of the next step to load
+  int64_t b = 0, m0 = 0, n0 = 0, rot = 0;
+  const char* a_base = nullptr;
+  const char* b_base = nullptr;
+  int64_t a_left0 = 0, b_left0 = 0;
+  const char* a_ptr = nullptr;
+  const char* b_ptr = nullptr;
+  int64_t a_left = 0, b_left = 0, k_left = 0;
+  int64_t ld_step = 0;  // walk position of the next step to load
+  auto seek = [&]() {
+    int64_t p = ld_step;
+    if (ld_step < nfull) {
+      p += rot;
+      p = p >= nfull ? p - nfull : p;
+    }
+    a_ptr = a_base + p * a_step;
+    a_left = a_left0 - p * a_step;
+    b_ptr = b_base + p * b_step;
+    b_left = b_left0 - p * b_step;
+    k_left = K - p * BK;
+  };
+  auto setup = [&](int64_t w) {
     int32_t pm, pn;
-    work_coords<8>(w0, total, args.tiles_m, args.tiles_n, b, pm, pn);
-    const int64_t m0 = (int64_t)pm * BM, n0 = (int64_t)pn * BN;
-    const int64_t rot = (args.rotate_k && nfull > 1) ? w0 % nfull : 0;
-    // source pointers / remaining bytes / K - k0 of the next step to load
-    const char* const a_base = (const char*)(args.A + b * args.sA + (A_KC ? m0 * lda : m0));
-    const char* const b_base = (const char*)(args.B + b * args.sB + (B_KC ? n0 * ldb : n0));
-    const int64_t a_left0 = A_KC ? ((M - 1 - m0) * lda + K) * 2 : ((K - 1) * lda + (M - m0)) * 2;
-    const int64_t b_left0 = B_KC ? ((N - 1 - n0) * ldb + K) * 2 : ((K - 1) * ldb + (N - n0)) * 2;
-    const char* a_ptr;
-    const char* b_ptr;
-    int64_t a_left, b_left, k_left;
-    int64_t ld_step = 0;  // walk position of the next step to load
-    auto seek = [&]() {
-      int64_t p = ld_step;
-      if (ld_step < nfull) {
-        p += rot;
-        p = p >= nfull ? p - nfull : p;
-      }
-      a_ptr = a_base + p * a_step;
-      a_left = a_left0 - p * a_step;
-      b_ptr = b_base + p * b_step;
-      b_left = b_left0 - p * b_step;
-      k_left = K - p * BK;
-    };
+    work_coords<8>(w, total, args.tiles_m, args.tiles_n, b, pm, pn);
+    m0 = (int64_t)pm * BM;
+    n0 = (int64_t)pn * BN;
+    rot = (args.rotate_k && nfull > 1) ? w % nfull : 0;
+    a_base = (const char*)(args.A + b * args.sA + (A_KC ? m0 * lda : m0));
+    b_base = (const char*)(args.B + b * args.sB + (B_KC ? n0 * ldb : n0));
+    a_left0 = A_KC ? ((M - 1 - m0) * lda + K) * 2 : ((K - 1) * lda + (M - m0)) * 2;
+    b_left0 = B_KC ? ((N - 1 - n0) * ldb + K) * 2 : ((K - 1) * ldb + (N - n0)) * 2;
+    ld_step = 0;
     seek();
+  };
+  bool prefetched = false;  // this item's prologue copies were issued by the previous item
+
+  for (int64_t w0 = blockIdx.x; w0 < total; w0 += gridDim.x) {
+    if (!prefetched) setup(w0);
 
     auto issue = [&](uint32_t buf, auto full) {
       const uint32_t st = lds0 + buf * STAGE;
@@ -507,10 +552,14 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
 
     if (nk > 0) {
       Frags<FM, FN> f[2];
+      if (prefetched) {
+        if constexpr (PERSIST_OK) wait_steps_plus<PER_STEP, ST, (D - 1 < 2 ? D - 1 : 2)>(min((int64_t)D, nk) - 1);
+      } else {
 #pragma unroll
-      for (int s = 0; s < D; ++s)
-        if (s < nk) issue((uint32_t)s, std::false_type{});
-      wait_steps<PER_STEP, true>(min((int64_t)D, nk) - 1);
+        for (int s = 0; s < D; ++s)
+          if (s < nk) issue((uint32_t)s, std::false_type{});
+        wait_steps<PER_STEP, true>(min((int64_t)D, nk) - 1);
+      }
       block_barrier();
       read(0, 0, f[0]);
 
@@ -545,7 +594,14 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
           if (ks + 1 < KS) {
             read(buf * STAGE, ks + 1, nxt);
           } else if (kt + 1 < nk) {
-            wait_steps<PER_STEP, !EARLY>(min((int64_t)(D - 2), nk - 2 - kt));
+            if (prefetched && kt + 1 < D) {
+              // stage kt+1 was issued before the previous item's ST stores,
+              // which may still be in flight behind it
+              if constexpr (PERSIST_OK)
+                wait_steps_plus<PER_STEP, ST, (D - 2 < 2 ? D - 2 : 2)>(min((int64_t)(D - 2), nk - 2 - kt));
+            } else {
+              wait_steps<PER_STEP, !EARLY>(min((int64_t)(D - 2), nk - 2 - kt));
+            }
             block_barrier();
             if (kt + D < nk) issue((uint32_t)((kt + D) % STAGES), std::false_type{});
             read((uint32_t)((kt + 1) % STAGES) * STAGE, 0, nxt);
@@ -557,6 +613,12 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
       // loads are all full K steps
       const int64_t nsteady = max((int64_t)0, min(nk, nfull) - D);
       int64_t kt = 0;
+      if (prefetched) {
+        // the first stages' waits must allow for the previous item's stores;
+        // one ring's worth of stages keeps the steady loop's buffers aligned
+        const int64_t head = min((int64_t)STAGES, nk);
+        for (; kt < head; ++kt) stage_dyn(kt);
+      }
       for (; kt + STAGES <= nsteady; kt += STAGES) {
         stage_const(std::integral_constant<uint32_t, 0>{});
         stage_const(std::integral_constant<uint32_t, 1>{});
@@ -567,21 +629,47 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
       for (; kt < nk; ++kt) stage_dyn(kt);
     }
 
+    // this item's origin (in persistent mode the state moves on below)
+    const int64_t cb = b, cm0 = m0, cn0 = n0;
+    prefetched = false;
+    if (persist && w0 + gridDim.x < total) {
+      // every wave's LDS reads of this item are done before the ring is
+      // refilled with the next item's first stages
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      block_barrier();
+      setup(w0 + gridDim.x);
+      if (nk > 0) {
+#pragma unroll
+        for (int s = 0; s < D; ++s)
+          if (s < nk) issue((uint32_t)s, std::false_type{});
+      }
+      prefetched = true;
+      asm volatile("" ::: "memory");
+    }
     {
-      const int64_t r0 = m0 + wm0, c0 = n0 + wn0;
-      char* Cb = (char*)args.C + b * args.sC * (int64_t)sizeof(Out);
+      const int64_t r0 = cm0 + wm0, c0 = cn0 + wn0;
+      char* Cb = (char*)args.C + cb * args.sC * (int64_t)sizeof(Out);
+      if (persist) {
+        // always ST store instructions (waves outside C store nothing: an
+        // empty descriptor drops every access)
+        const bool in = r0 < M && c0 < N;
+        store_tile_vec<Out, FM, FN>(in ? Cb + (r0 * args.ldc + c0) * (int64_t)sizeof(Out) : Cb,
+                                    in ? ((M - 1 - r0) * args.ldc + (N - c0)) * (int64_t)sizeof(Out) : 0, args.ldc,
+                                    in ? N - c0 : 0, lane, acc);
+        goto stored;
+      }
       if constexpr (EPI_PASSES > 0) {
         if (N % (16 / (int)sizeof(Out)) == 0) {  // uniform over the work-group
           // every wave's reads of the last stage are done before LDS is reused
           __builtin_amdgcn_s_waitcnt(0xC07F);
           block_barrier();
           store_tile_lds<Out, BM, BN, WM, WN, FM, FN, EPI_PASSES, 0>(
-              lds, Cb + (m0 * args.ldc + n0) * (int64_t)sizeof(Out),
-              ((M - 1 - m0) * args.ldc + (N - n0)) * (int64_t)sizeof(Out), args.ldc, N - n0, wave, lane, acc);
+              lds, Cb + (cm0 * args.ldc + cn0) * (int64_t)sizeof(Out),
+              ((M - 1 - cm0) * args.ldc + (N - cn0)) * (int64_t)sizeof(Out), args.ldc, N - cn0, wave, lane, acc);
           goto stored;
         }
       }
-      if (N % 4 == 0 || n0 + BN <= N) {
+      if (N % 4 == 0 || cn0 + BN <= N) {
         if (r0 < M && c0 < N)
           store_tile_vec<Out, FM, FN>(Cb + (r0 * args.ldc + c0) * (int64_t)sizeof(Out),
                                       ((M - 1 - r0) * args.ldc + (N - c0)) * (int64_t)sizeof(Out), args.ldc, N - c0,
@@ -591,7 +679,7 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
       }
     stored:;
     }
-    if (w0 + gridDim.x < total) {
+    if (!persist && w0 + gridDim.x < total) {
       // the next tile's prologue overwrites buffers other waves may still read
       wait_vmcnt<0>();
       block_barrier();

@@ -40,6 +40,10 @@ constexpr TileShape kTiles[] = {
     {128, 128, 32, 2, 2, 3, 3},  // 17: 48 KiB
     {64, 128, 64, 2, 2, 2, 3},   // 18: 32x64 per wave, 48 KiB
     {128, 64, 64, 2, 2, 2, 4},   // 19: 64x32 per wave, 32 KiB
+    // 5-deep rings (160 KiB): three K steps between a stage's copies and
+    // their use -- a single wave per SIMD has nothing else to hide latency
+    {256, 256, 32, 2, 2, 5},     // 20: 4 waves, 128x128 per wave
+    {256, 256, 32, 2, 4, 5},     // 21: 8 waves, 128x64 per wave
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -50,6 +54,18 @@ constexpr TileShape kGenericTiles[] = {
 constexpr int kNumGeneric = sizeof(kGenericTiles) / sizeof(kGenericTiles[0]);
 
 constexpr int lds_bytes_of(const TileShape& t) { return t.stages * (t.bm * t.bk + t.bk * t.bn) * 2; }
+
+// Whether the tile kernel can run persistently: the first wait of a
+// prefetched item counts the copy instructions of the stages after the first
+// one plus the item's store instructions, and that count must fit the 6-bit
+// vector-memory counter.
+constexpr bool persist_ok(const TileShape& t) {
+  const int copy_waves = t.dw ? t.dw : t.wm * t.wn;
+  const int per_step = (t.bm * t.bk * 2 / 1024) / copy_waves + (t.bk * t.bn * 2 / 1024) / copy_waves;
+  const int d = t.stages >= 3 ? t.stages - 1 : t.stages;
+  const int stores = (t.bm / t.wm / 32) * (t.bn / t.wn / 32) * 4;
+  return (d - 1) * per_step + stores < 64;
+}
 
 // Skinny (M <= 32) streaming kernel: MB 16-row blocks of A and C, NB 16-row
 // blocks of B (16*NB columns of C) per work-group, WAVES waves, STAGES LDS

@@ -179,3 +179,38 @@ def test_batched_broadcast_and_strides():
     torch.cuda.synchronize()
     ref = oracle.gemm(A, B, m=m, n=n, k=k, batch=batch, stride_a=m * k, stride_b=0)
     check(values(C), ref, tol_fp32(k, oracle.max_abs(A), oracle.max_abs(B)), "fp32", "broadcast B")
+
+
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 1), (0, 1)])
+def test_persistent_launch_matches_one_workgroup_per_tile(ta, tb):
+    """Persistent work-groups (each loops over tiles and issues the next
+    tile's first copies before this tile's stores) compute exactly what one
+    work-group per tile computes -- the K walk and the summation order are the
+    same -- on ragged batched shapes with enough tiles that the launcher does
+    loop, with a masked K tail and with a K of several ring lengths."""
+    rng = np.random.default_rng(77)
+    # 160 matrices of 264 x 264: >= 2 items per resident work-group for every tile below
+    # (e.g. 4 256x256 tiles x 160 = 640 > 2 x 256), so the launcher does loop
+    for (m, n, k, batch) in [(264, 264, 96, 160), (264, 264, 1000, 160)]:
+        ar, ac = (k, m) if ta else (m, k)
+        br, bc = (n, k) if tb else (k, n)
+        A = synth.draw(rng, (batch, ar, ac), "normal", 1.0)
+        B = synth.draw(rng, (batch, br, bc), "normal", 1.0)
+        Ag, Bg = to_gpu(A), to_gpu(B)
+        base = tg.plan(m, n, k, trans_a=ta, trans_b=tb, out_dtype=torch.float32, batch=batch)
+        idx = synth.sample_indices(5, batch, m, n, count=2048)
+        ref = oracle.gemm(A, B, m=m, n=n, k=k, trans_a=ta, trans_b=tb, batch=batch, stride_a=ar * ac,
+                          stride_b=br * bc, idx=idx)
+        t = tol_fp32(k, oracle.max_abs(A), oracle.max_abs(B))
+        for tile in (0, 1, 8, 13):
+            outs = []
+            for persist in (True, False):
+                pl = tg.plan_tile(base, tg.VARIANT_TILE, tile)
+                pl.flags = (pl.flags | tg.FLAG_PERSIST) if persist else (pl.flags & ~tg.FLAG_PERSIST)
+                C = torch.full((batch, m, n), CANARY, dtype=torch.float32, device="cuda")
+                tg.bmm_run(pl, batch, ar * ac, br * bc, m * n, Ag, Bg, C)
+                torch.cuda.synchronize()
+                outs.append(C.cpu().numpy())
+            what = f"persistent tile={tile} m={m} n={n} k={k} batch={batch} ta={ta} tb={tb}"
+            assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32)), what
+            check(outs[0][idx[:, 0], idx[:, 1], idx[:, 2]].astype(np.float64), ref, t, "fp32", what)
