@@ -251,11 +251,18 @@ def cpu_baseline(p, unit, seconds):
     import oracle
     import synth
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    calib = synth.sample_indices(77, p.batch, p.m, p.n, count=256, edges=())
-    t0 = time.perf_counter()
-    oracle.gemm_problem(p, idx=calib)
-    dt = max(time.perf_counter() - t0, 1e-4)
-    count = int(max(256, min(50_000_000, 256 * seconds / dt)))
+    # size the sample from timed trial runs that grow until they take long
+    # enough to be measured without thread start-up dominating
+    count, dt = 4096, 0.0
+    while True:
+        calib = synth.sample_indices(77, p.batch, p.m, p.n, count=count, edges=())
+        t0 = time.perf_counter()
+        oracle.gemm_problem(p, idx=calib)
+        dt = max(time.perf_counter() - t0, 1e-4)
+        if dt >= 0.5 or count >= 50_000_000:
+            break
+        count = min(50_000_000, count * 8)
+    count = int(max(256, min(50_000_000, count * seconds / dt)))
     idx = synth.sample_indices(78, p.batch, p.m, p.n, count=count, edges=())
     t0 = time.perf_counter()
     oracle.gemm_problem(p, idx=idx)
