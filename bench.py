@@ -67,7 +67,9 @@ def main():
                          "default 4 for HBM-bound workloads, 1 otherwise")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile", type=int, default=None, help="override the planner's tile (same variant)")
-    ap.add_argument("--no-persist", action="store_true", help="clear the plan's persistent-launch flag")
+    ap.add_argument("--no-persist", action="store_true", help="clear the plan's persistent-launch flags")
+    ap.add_argument("--no-prefetch", action="store_true", help="clear the plan's prefetch flag")
+    ap.add_argument("--prefetch", action="store_true", help="set the plan's persistent and prefetch flags")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to calibrate FETCH_SIZE/WRITE_SIZE)")
@@ -119,7 +121,11 @@ def main():
         if args.tile is not None:
             pl = tg.plan_tile(pl, pl.variant, args.tile)
         if args.no_persist:
-            pl.flags &= ~tg.FLAG_PERSIST
+            pl.flags &= ~(tg.FLAG_PERSIST | tg.FLAG_PREFETCH)
+        if args.no_prefetch:
+            pl.flags &= ~tg.FLAG_PREFETCH
+        if args.prefetch:
+            pl.flags |= tg.FLAG_PERSIST | tg.FLAG_PREFETCH
         B = Bs[i % len(Bs)]
         C = Cs[i % len(Cs)]
         if p.batch == 1:

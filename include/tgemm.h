@@ -65,9 +65,11 @@ typedef enum {
 #define TG_FLAG_ROTATE_K 0x4 /* tile kernel: work-groups start their K walks at different steps */
 #define TG_FLAG_PERSIST 0x8  /* tile kernel: when there are more tiles than resident work-groups,
                                 launch one work-group per resident slot and let each loop over
-                                tiles, issuing the next tile's first copies before this tile's
-                                stores.  A caller may clear this flag (or ROTATE_K) in a plan;
-                                the result is the same up to fp32 summation order. */
+                                tiles (no dispatch gap between tiles) */
+#define TG_FLAG_PREFETCH 0x10 /* with PERSIST: issue the next tile's first copies before this
+                                 tile's stores (stores go straight from registers).  A caller may
+                                 clear PERSIST, PREFETCH or ROTATE_K in a plan; the result is the
+                                 same up to fp32 summation order. */
 
 /*
  * A plan: caller-owned plain data, filled by gemm_plan(), read by gemm_run()

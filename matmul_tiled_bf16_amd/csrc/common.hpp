@@ -27,7 +27,7 @@ struct GemmArgs {
   int64_t batch;
   int32_t tiles_m, tiles_n;
   int32_t rotate_k;  // nonzero: each work-group starts its walk over K at a different step
-  int32_t persist;   // nonzero: work-groups loop over items, prefetching the next one's first stages
+  int32_t persist;   // nonzero: the next item's first stages are issued before this item's stores
 };
 
 using KernelFn = void (*)(GemmArgs);

@@ -134,16 +134,19 @@ void fill_shape(gemm_plan_t* p) {
   // of its own, and lock-step walks would crowd the same HBM channels.
   const bool rotate = p->variant == TG_VARIANT_TILE && (p->tiles_m == 1 || p->tiles_n == 1);
   p->flags = (p->flags & ~TG_FLAG_ROTATE_K) | (rotate ? TG_FLAG_ROTATE_K : 0);
-  // Persistent launches store straight from registers, 4 columns at a time.
-  // They pay off where the MFMA work per tile dwarfs its memory traffic (no
-  // work-group launch gap, the next tile's first copies overlap this tile's
-  // stores); HBM-bound shapes keep one work-group per tile and the LDS-staged
+  // Persistent launches: work-groups that loop over tiles keep their CU
+  // slot, where short-lived ones measured idle slots waiting for dispatch.
+  // Prefetching the next tile during this tile's stores pays off where the
+  // MFMA work per tile dwarfs its memory traffic; it stores straight from
+  // registers, 4 columns at a time.  HBM-bound shapes keep the LDS-staged
   // row-segment stores, which measured faster for them.
   const double flops = 2.0 * (double)p->m * (double)p->n * (double)p->k;
   const double bytes = 2.0 * ((double)p->m * p->k + (double)p->k * p->n) +
                        (p->out_type == TG_FP32 ? 4.0 : 2.0) * (double)p->m * p->n;
-  const bool persist = p->variant == TG_VARIANT_TILE && p->n % 4 == 0 && bytes > 0 && flops / bytes > 312.5;
-  p->flags = (p->flags & ~TG_FLAG_PERSIST) | (persist ? TG_FLAG_PERSIST : 0);
+  const bool persist = p->variant == TG_VARIANT_TILE;
+  const bool prefetch = persist && p->n % 4 == 0 && bytes > 0 && flops / bytes > 312.5;
+  p->flags = (p->flags & ~(TG_FLAG_PERSIST | TG_FLAG_PREFETCH)) | (persist ? TG_FLAG_PERSIST : 0) |
+             (prefetch ? TG_FLAG_PREFETCH : 0);
 }
 
 }  // namespace
@@ -338,12 +341,18 @@ static tg_status launch(const gemm_plan_t* plan, int64_t batch, int64_t sA, int6
     // keeps every item on the XCD the kernel's tile order assumes)
     const int64_t total = groups * batch;
     int64_t cap = (int64_t)1 << 30;
-    if (variant == TG_VARIANT_TILE && (p.flags & TG_FLAG_PERSIST) && p.n % 4 == 0 && tg::persist_ok(kTiles[tile])) {
+    if (variant == TG_VARIANT_TILE && (p.flags & TG_FLAG_PERSIST)) {
       // persistent: one work-group per resident slot (a multiple of 8)
       const int64_t slots = (int64_t)compute_units() * kTiles[tile].occ;
       if (slots > 0 && total >= 2 * slots) {
         cap = slots;
-        a.persist = 1;
+        const int out_size = p.out_type == TG_FP32 ? 4 : 2;
+        if (p.flags & TG_FLAG_PREFETCH) {
+          if (tg::split_ok(kTiles[tile], out_size) && p.n % (16 / out_size) == 0)
+            a.persist = 2;  // copy waves prefetch, the others store through LDS
+          else if (p.n % 4 == 0 && tg::persist_ok(kTiles[tile]))
+            a.persist = 1;  // every wave prefetches, then stores from registers
+        }
       }
     }
     grid = dim3((unsigned)(total < cap ? total : cap), 1);

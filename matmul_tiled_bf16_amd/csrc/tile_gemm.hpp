@@ -242,61 +242,99 @@ __device__ __forceinline__ void store_tile_vec(const void* Ctile, int64_t bytes,
 // Rows past M are dropped by the descriptor's size; 16-byte units at or past
 // column N get an out-of-range offset (the caller guarantees N is a multiple
 // of 16 / sizeof(Out)).
+// LDS layout of a staged C band: rows of BN*sizeof(Out) bytes split into
+// 16-byte units; unit u of row r sits at position u ^ (r & SM).
+template <typename Out, int BN>
+struct StagedC {
+  static constexpr uint32_t es = sizeof(Out);
+  static constexpr uint32_t ROWB = BN * es;  // bytes of one tile row
+  static constexpr int UPR = ROWB / 16;      // 16-byte units per row
+  static constexpr int SM = (UPR < 16 ? UPR : 16) - 1;
+  static __device__ __forceinline__ uint32_t pos(int r, uint32_t byte) {
+    return (uint32_t)r * ROWB + ((((byte >> 4) ^ (uint32_t)(r & SM))) << 4) + (byte & 15);
+  }
+};
+
+// Waves whose rows fall in band `pass` (RP rows) write their blocks, already
+// converted to Out, into the band's LDS image.
+template <typename Out, int BM, int BN, int WM, int WN, int FM, int FN, int RP>
+__device__ __forceinline__ void stage_c_write(TG_LDS char* lds, int pass, int wave, int lane,
+                                              const f32x16 (&acc)[FM][FN]) {
+  using L = StagedC<Out, BN>;
+  const int li = lane & 31, lg = lane >> 5;
+  const int wr = wave / WN, wn0 = (wave % WN) * (BN / WN);
+  if (wr * (BM / WM) / RP != pass) return;
+  const int rbase = wr * (BM / WM) - pass * RP;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int r = rbase + i * 32 + li;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = wn0 + j * 32 + 8 * g + 4 * lg;  // 4 consecutive columns
+        const uint32_t at = L::pos(r, (uint32_t)col * L::es);
+        const f32x16& a = acc[i][j];
+        if constexpr (L::es == 4) {
+          *(TG_LDS u32x4*)(lds + at) =
+              __builtin_bit_cast(u32x4, f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]});
+        } else {
+          *(TG_LDS u32x2*)(lds + at) =
+              u32x2{pack2<Out>(a[4 * g], a[4 * g + 1]), pack2<Out>(a[4 * g + 2], a[4 * g + 3])};
+        }
+      }
+    }
+  }
+}
+
+// Threads t = 0 .. NT-1 store the band: each reads 16 consecutive bytes of a
+// row and writes them, so one store instruction covers 1 KiB of row segments.
+template <typename Out, int BN, int RP, int NT, int AUX>
+__device__ __forceinline__ void stage_c_store(const TG_LDS char* lds, __amdgpu_buffer_rsrc_t rs, int64_t ldc,
+                                              int64_t n_left, int pass, int t) {
+  using L = StagedC<Out, BN>;
+  constexpr int UNITS = RP * L::UPR;
+  static_assert(UNITS % NT == 0, "band splits evenly over the storing threads");
+#pragma unroll
+  for (int k = 0; k < UNITS / NT; ++k) {
+    const int idx = k * NT + t;
+    const int r = idx / L::UPR, p = idx % L::UPR;
+    const u32x4 v = *(const TG_LDS u32x4*)(lds + (uint32_t)r * L::ROWB + (uint32_t)p * 16);
+    const int u = p ^ (r & L::SM);
+    const int col = u * (16 / L::es);
+    const uint32_t off =
+        col < n_left ? (uint32_t)((pass * RP + r) * ldc) * L::es + (uint32_t)col * L::es : kOutOfRange;
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, AUX);
+  }
+}
+
+// LDS-staged store of the work-group's BM x BN tile ("Triton Optimization
+// Reference", section 5: the epilogue goes out in subtiles through shared
+// memory).  The MFMA result layout gives each lane four consecutive columns
+// of one row, so direct stores write 32 rows x 32 bytes per instruction --
+// a scattered pattern the memory system handles poorly.  Here the waves
+// first write their blocks (already converted to Out) into LDS, then every
+// thread reads 16 consecutive bytes of a row and stores them, so one store
+// instruction covers 1 KiB of whole row segments of C.  The XOR placement of
+// 16-byte units keeps the writes of 16 rows on distinct banks; the readers
+// undo it when they form the global column.  When the tile does not fit the
+// LDS the kernel owns, it goes in PASSES row bands, one row of waves per
+// band.  Rows past M are dropped by the descriptor's size; 16-byte units at
+// or past column N get an out-of-range offset (the caller guarantees N is a
+// multiple of 16 / sizeof(Out)).
 template <typename Out, int BM, int BN, int WM, int WN, int FM, int FN, int PASSES, int AUX>
 __device__ __forceinline__ void store_tile_lds(TG_LDS char* lds, void* Ctile, int64_t bytes, int64_t ldc,
                                                int64_t n_left, int wave, int lane, const f32x16 (&acc)[FM][FN]) {
   constexpr int NT = WM * WN * 64;
-  constexpr uint32_t es = sizeof(Out);
-  constexpr uint32_t ROWB = BN * es;          // bytes of one tile row
-  constexpr int UPR = ROWB / 16;              // 16-byte units per row
-  constexpr int SM = (UPR < 16 ? UPR : 16) - 1;
-  constexpr int RP = BM / PASSES;             // rows per band
-  constexpr int UNITS = RP * UPR;             // units per band
-  static_assert(UPR >= 4 && UNITS % NT == 0 && RP % (BM / WM) == 0, "epilogue band shape");
+  constexpr int RP = BM / PASSES;  // rows per band
+  static_assert(StagedC<Out, BN>::UPR >= 4 && RP % (BM / WM) == 0, "epilogue band shape");
   const __amdgpu_buffer_rsrc_t rs = store_rsrc(Ctile, bytes);
-  const int li = lane & 31, lg = lane >> 5;
-  const int wr = wave / WN, wn0 = (wave % WN) * (BN / WN);
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
-    // waves whose rows fall in this band write them, converted, into LDS
-    if (wr * (BM / WM) / RP == pass) {
-      const int rbase = wr * (BM / WM) - pass * RP;
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = rbase + i * 32 + li;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int col = wn0 + j * 32 + 8 * g + 4 * lg;  // 4 consecutive columns
-            const uint32_t byte = (uint32_t)col * es;
-            const uint32_t pos = (uint32_t)r * ROWB + ((((byte >> 4) ^ (uint32_t)(r & SM))) << 4) + (byte & 15);
-            const f32x16& a = acc[i][j];
-            if constexpr (es == 4) {
-              *(TG_LDS u32x4*)(lds + pos) =
-                  __builtin_bit_cast(u32x4, f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]});
-            } else {
-              *(TG_LDS u32x2*)(lds + pos) =
-                  u32x2{pack2<Out>(a[4 * g], a[4 * g + 1]), pack2<Out>(a[4 * g + 2], a[4 * g + 3])};
-            }
-          }
-        }
-      }
-    }
+    stage_c_write<Out, BM, BN, WM, WN, FM, FN, RP>(lds, pass, wave, lane, acc);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
     block_barrier();
-    // every thread stores whole 16-byte units of rows, 1 KiB per instruction
-#pragma unroll
-    for (int k = 0; k < UNITS / NT; ++k) {
-      const int idx = k * NT + wave * 64 + lane;
-      const int r = idx / UPR, p = idx % UPR;
-      const u32x4 v = *(const TG_LDS u32x4*)(lds + (uint32_t)r * ROWB + (uint32_t)p * 16);
-      const int u = p ^ (r & SM);
-      const int col = u * (16 / es);
-      const uint32_t off =
-          col < n_left ? (uint32_t)((pass * RP + r) * ldc) * es + (uint32_t)col * es : kOutOfRange;
-      __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, AUX);
-    }
+    stage_c_store<Out, BN, RP, NT, AUX>(lds, rs, ldc, n_left, pass, wave * 64 + lane);
     if (pass + 1 < PASSES) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // this band's LDS reads are done before the next band's writes
       block_barrier();
@@ -411,7 +449,16 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
   // stores, a fixed count per wave -- stay outstanding.
   constexpr int ST = FM * FN * 4;  // store instructions of store_tile_vec
   constexpr bool PERSIST_OK = (D - 1) * PER_STEP + ST < 64;  // fits the counter
-  const bool persist = PERSIST_OK && args.persist != 0;
+  // Split mode (args.persist == 2, kernels with dedicated copy waves): the
+  // tile is staged through the ring's LDS and only the waves that issue no
+  // copies store it.  A copy wave's counter then never holds stores, so it
+  // prefetches the next item as soon as the storing waves have read the
+  // staged tile, and no wait of the next item involves the stores at all.
+  constexpr int NS = NW - DW;  // waves that never copy
+  constexpr bool SPLIT_OK =
+      NS > 0 && EPI_PASSES == 1 && ((BM * StagedC<Out, BN>::UPR) % (NS * 64) == 0);
+  const bool persist = PERSIST_OK && args.persist == 1;
+  const bool split = SPLIT_OK && args.persist == 2;
   // the item being computed: matrix, tile origin, walk rotation, and the
   // source pointers / remaining bytes / K - k0 of the next step to load
   int64_t b = 0, m0 = 0, n0 = 0, rot = 0;
@@ -448,6 +495,7 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
     seek();
   };
   bool prefetched = false;  // this item's prologue copies were issued by the previous item
+  bool behind_stores = false;  // ... and this wave's stores of that item were issued after them
 
   for (int64_t w0 = blockIdx.x; w0 < total; w0 += gridDim.x) {
     if (!prefetched) setup(w0);
@@ -552,13 +600,17 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
 
     if (nk > 0) {
       Frags<FM, FN> f[2];
-      if (prefetched) {
-        if constexpr (PERSIST_OK) wait_steps_plus<PER_STEP, ST, (D - 1 < 2 ? D - 1 : 2)>(min((int64_t)D, nk) - 1);
-      } else {
+      if (!prefetched) {
 #pragma unroll
         for (int s = 0; s < D; ++s)
           if (s < nk) issue((uint32_t)s, std::false_type{});
+      }
+      if (behind_stores) {
+        if constexpr (PERSIST_OK) wait_steps_plus<PER_STEP, ST, (D - 1 < 2 ? D - 1 : 2)>(min((int64_t)D, nk) - 1);
+      } else if (copier) {
         wait_steps<PER_STEP, true>(min((int64_t)D, nk) - 1);
+      } else {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // no copies of its own: only its LDS reads
       }
       block_barrier();
       read(0, 0, f[0]);
@@ -577,7 +629,8 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
             slice(cur, &nxt, buf * STAGE, ks + 1, nullptr, nullptr, 0, 0, 0);
           } else {
             // copies for stages kt+2 .. kt+D-1 may stay in flight
-            wait_vmcnt<(D - 2) * PER_STEP, !EARLY>();
+            if (DW == NW || copier) wait_vmcnt<(D - 2) * PER_STEP, !EARLY>();
+            else if constexpr (!EARLY) __builtin_amdgcn_s_waitcnt(0xC07F);
             block_barrier();
             slice(cur, &nxt, ((buf + 1) % STAGES) * STAGE, 0, &rsa, &rsb, lds0 + dst, 0, PER_STEP);
           }
@@ -594,13 +647,15 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
           if (ks + 1 < KS) {
             read(buf * STAGE, ks + 1, nxt);
           } else if (kt + 1 < nk) {
-            if (prefetched && kt + 1 < D) {
+            if (behind_stores && kt + 1 < D) {
               // stage kt+1 was issued before the previous item's ST stores,
               // which may still be in flight behind it
               if constexpr (PERSIST_OK)
                 wait_steps_plus<PER_STEP, ST, (D - 2 < 2 ? D - 2 : 2)>(min((int64_t)(D - 2), nk - 2 - kt));
-            } else {
+            } else if (DW == NW || copier) {
               wait_steps<PER_STEP, !EARLY>(min((int64_t)(D - 2), nk - 2 - kt));
+            } else if constexpr (!EARLY) {
+              __builtin_amdgcn_s_waitcnt(0xC07F);
             }
             block_barrier();
             if (kt + D < nk) issue((uint32_t)((kt + D) % STAGES), std::false_type{});
@@ -613,7 +668,7 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
       // loads are all full K steps
       const int64_t nsteady = max((int64_t)0, min(nk, nfull) - D);
       int64_t kt = 0;
-      if (prefetched) {
+      if (behind_stores) {
         // the first stages' waits must allow for the previous item's stores;
         // one ring's worth of stages keeps the steady loop's buffers aligned
         const int64_t head = min((int64_t)STAGES, nk);
@@ -632,6 +687,39 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
     // this item's origin (in persistent mode the state moves on below)
     const int64_t cb = b, cm0 = m0, cn0 = n0;
     prefetched = false;
+    behind_stores = false;
+    if constexpr (SPLIT_OK) {
+      if (split) {
+        using L = StagedC<Out, BN>;
+        char* Cb = (char*)args.C + cb * args.sC * (int64_t)sizeof(Out);
+        // every wave's reads of the ring are done; stage the tile in it
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        block_barrier();
+        stage_c_write<Out, BM, BN, WM, WN, FM, FN, BM>(lds, 0, wave, lane, acc);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        block_barrier();
+        if (!copier) {
+          const __amdgpu_buffer_rsrc_t rs =
+              store_rsrc(Cb + (cm0 * args.ldc + cn0) * (int64_t)L::es, ((M - 1 - cm0) * args.ldc + (N - cn0)) * (int64_t)L::es);
+          stage_c_store<Out, BN, BM, NS * 64, 0>(lds, rs, args.ldc, N - cn0, 0, wave * 64 + lane);
+        }
+        // the staged tile has been read (the stores themselves may still be
+        // in flight) before the copy waves refill the ring
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        block_barrier();
+        if (w0 + gridDim.x < total) {
+          setup(w0 + gridDim.x);
+          if (nk > 0) {
+#pragma unroll
+            for (int s = 0; s < D; ++s)
+              if (s < nk) issue((uint32_t)s, std::false_type{});
+          }
+          prefetched = true;
+        }
+        asm volatile("" ::: "memory");
+        continue;
+      }
+    }
     if (persist && w0 + gridDim.x < total) {
       // every wave's LDS reads of this item are done before the ring is
       // refilled with the next item's first stages
@@ -644,6 +732,7 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
           if (s < nk) issue((uint32_t)s, std::false_type{});
       }
       prefetched = true;
+      behind_stores = true;
       asm volatile("" ::: "memory");
     }
     {

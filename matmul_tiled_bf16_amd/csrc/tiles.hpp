@@ -44,6 +44,9 @@ constexpr TileShape kTiles[] = {
     // their use -- a single wave per SIMD has nothing else to hide latency
     {256, 256, 32, 2, 2, 5},     // 20: 4 waves, 128x128 per wave
     {256, 256, 32, 2, 4, 5},     // 21: 8 waves, 128x64 per wave
+    // 8 waves, 4 of them copy: persistent work-groups whose copy waves
+    // prefetch while the other waves store (split mode)
+    {128, 128, 64, 2, 4, 2, 2, 4},  // 22: 64x32 per wave, 64 KiB
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -59,6 +62,17 @@ constexpr int lds_bytes_of(const TileShape& t) { return t.stages * (t.bm * t.bk 
 // prefetched item counts the copy instructions of the stages after the first
 // one plus the item's store instructions, and that count must fit the 6-bit
 // vector-memory counter.
+// Whether the tile kernel can run in split mode for a given output element
+// size: dedicated copy waves, a C tile that fits the ring's LDS in one band,
+// and a band that divides evenly over the waves that store it.
+constexpr bool split_ok(const TileShape& t, int out_size) {
+  const int nw = t.wm * t.wn;
+  const int stores = nw - (t.dw ? t.dw : nw);
+  const int c_bytes = t.bm * t.bn * out_size;
+  return stores > 0 && t.bn * out_size / 16 >= 4 && c_bytes <= lds_bytes_of(t) &&
+         (c_bytes / 16) % (stores * 64) == 0;
+}
+
 constexpr bool persist_ok(const TileShape& t) {
   const int copy_waves = t.dw ? t.dw : t.wm * t.wn;
   const int per_step = (t.bm * t.bk * 2 / 1024) / copy_waves + (t.bk * t.bn * 2 / 1024) / copy_waves;

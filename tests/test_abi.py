@@ -167,12 +167,12 @@ def test_plan_choices_for_the_workloads():
         p = tg.plan(mm, nn, kk, trans_b=tb, batch=128)
         assert (p.variant, p.bm, p.bn) == (tg.VARIANT_TILE, 128, 128)
         assert bool(p.flags & tg.FLAG_ROTATE_K) == (nn == 128)
-        assert not p.flags & tg.FLAG_PERSIST       # HBM-bound: one work-group per tile
+        assert p.flags & tg.FLAG_PERSIST and not p.flags & tg.FLAG_PREFETCH  # HBM-bound: LDS-staged stores
     with pytest.raises(tg.TgError):
         tg.plan(64, 64, 64, batch=0)
     p = tg.plan(8192, 8192, 8192, out_dtype=torch.bfloat16)
     assert (p.variant, p.bm, p.bn, p.wg_threads) == (tg.VARIANT_TILE, 256, 256, 512) and p.tiles_m * p.tiles_n == 1024
-    assert p.flags & tg.FLAG_PERSIST                # MFMA-bound: persistent work-groups
+    assert p.flags & tg.FLAG_PERSIST and p.flags & tg.FLAG_PREFETCH  # MFMA-bound: prefetch during stores
     assert p.workspace_bytes == 0
 
 

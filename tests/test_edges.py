@@ -181,14 +181,17 @@ def test_batched_broadcast_and_strides():
     check(values(C), ref, tol_fp32(k, oracle.max_abs(A), oracle.max_abs(B)), "fp32", "broadcast B")
 
 
-@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 1), (0, 1)])
-def test_persistent_launch_matches_one_workgroup_per_tile(ta, tb):
-    """Persistent work-groups (each loops over tiles and issues the next
-    tile's first copies before this tile's stores) compute exactly what one
+@pytest.mark.parametrize("ta,tb,out_dtype", [(0, 0, "fp32"), (1, 1, "fp32"), (0, 1, "fp32"), (0, 1, "bf16")])
+def test_persistent_launch_matches_one_workgroup_per_tile(ta, tb, out_dtype):
+    """Persistent work-groups (each loops over tiles; with PREFETCH the next
+    tile's first copies are issued before this tile's stores -- by every wave,
+    or, for kernels with dedicated copy waves, by the copy waves while the
+    other waves store the tile through LDS) compute exactly what one
     work-group per tile computes -- the K walk and the summation order are the
     same -- on ragged batched shapes with enough tiles that the launcher does
     loop, with a masked K tail and with a K of several ring lengths."""
     rng = np.random.default_rng(77)
+    tout = torch_out_dtype(out_dtype)
     # 160 matrices of 264 x 264: >= 2 items per resident work-group for every tile below
     # (e.g. 4 256x256 tiles x 160 = 640 > 2 x 256), so the launcher does loop
     for (m, n, k, batch) in [(264, 264, 96, 160), (264, 264, 1000, 160)]:
@@ -197,20 +200,24 @@ def test_persistent_launch_matches_one_workgroup_per_tile(ta, tb):
         A = synth.draw(rng, (batch, ar, ac), "normal", 1.0)
         B = synth.draw(rng, (batch, br, bc), "normal", 1.0)
         Ag, Bg = to_gpu(A), to_gpu(B)
-        base = tg.plan(m, n, k, trans_a=ta, trans_b=tb, out_dtype=torch.float32, batch=batch)
+        base = tg.plan(m, n, k, trans_a=ta, trans_b=tb, out_dtype=tout, batch=batch)
         idx = synth.sample_indices(5, batch, m, n, count=2048)
         ref = oracle.gemm(A, B, m=m, n=n, k=k, trans_a=ta, trans_b=tb, batch=batch, stride_a=ar * ac,
                           stride_b=br * bc, idx=idx)
         t = tol_fp32(k, oracle.max_abs(A), oracle.max_abs(B))
-        for tile in (0, 1, 8, 13):
+        # 0, 1, 8, 13: every wave copies; 15, 22: dedicated copy waves (22: split mode)
+        for tile in (0, 1, 8, 13, 15, 22):
             outs = []
-            for persist in (True, False):
+            both = tg.FLAG_PERSIST | tg.FLAG_PREFETCH
+            for flags in (both, tg.FLAG_PERSIST, 0):
                 pl = tg.plan_tile(base, tg.VARIANT_TILE, tile)
-                pl.flags = (pl.flags | tg.FLAG_PERSIST) if persist else (pl.flags & ~tg.FLAG_PERSIST)
-                C = torch.full((batch, m, n), CANARY, dtype=torch.float32, device="cuda")
+                pl.flags = (pl.flags & ~both) | flags
+                C = torch.full((batch, m, n), CANARY, dtype=tout, device="cuda")
                 tg.bmm_run(pl, batch, ar * ac, br * bc, m * n, Ag, Bg, C)
                 torch.cuda.synchronize()
-                outs.append(C.cpu().numpy())
-            what = f"persistent tile={tile} m={m} n={n} k={k} batch={batch} ta={ta} tb={tb}"
-            assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32)), what
-            check(outs[0][idx[:, 0], idx[:, 1], idx[:, 2]].astype(np.float64), ref, t, "fp32", what)
+                outs.append((bits(C), values(C)))
+            what = f"persistent tile={tile} m={m} n={n} k={k} batch={batch} ta={ta} tb={tb} out={out_dtype}"
+            for o in outs[1:]:
+                assert np.array_equal(outs[0][0], o[0]), what
+            got = outs[0][1][idx[:, 0], idx[:, 1], idx[:, 2]]
+            check(got, ref, t, out_dtype, what)
