@@ -10,7 +10,10 @@ this file only builds it with gcc and marshals numpy arrays through ctypes.
 
 What it follows: C[b] = op(A[b]) op(B[b]) with op() a stride swap and the batch
 a per-operand base offset (p1 "Triton Optimization Reference" sections 2 and 3;
-p2 "Optimize Triton Block Parameters" Step 1 for the 2*M*N*K flop count).
+p2 "Optimize Triton Block Parameters" Step 1 for the 2*M*N*K flop count); and,
+for the fused attention forward pass, O = softmax(scale * Q K^T) V row by row
+with no mask (``oracle_attention.c``; p1's opening section names attention as
+the companion of its GEMM/BMM patterns).
 """
 from __future__ import annotations
 
@@ -23,6 +26,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle_gemm.c")
+_SRC_ATTN = os.path.join(_HERE, "oracle_attention.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 IN_TYPES = {"bf16": 0, "fp16": 1}
@@ -31,9 +35,10 @@ _lib = None
 
 def build(force: bool = False) -> str:
     """Compile liboracle.so with gcc (host only, no HIP)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(_SRC_ATTN))
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < newest:
         tmp = _LIB + f".tmp{os.getpid()}"
-        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, _SRC_ATTN, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -55,6 +60,9 @@ def _load():
         lib.oracle_decode.argtypes = [ctypes.c_int, p, i64, p]
         lib.oracle_round.restype = None
         lib.oracle_round.argtypes = [ctypes.c_int, p, i64, p]
+        lib.oracle_attention.restype = ctypes.c_int
+        lib.oracle_attention.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.c_double, p, i64, i64, p, i64, i64,
+                                         p, i64, i64, i64, p, i64, p]
         _lib = lib
     return _lib
 
@@ -95,6 +103,32 @@ def gemm(A: np.ndarray, B: np.ndarray, *, m: int, n: int, k: int, trans_a: int =
     if rc != 0:
         raise IndexError("oracle_gemm: sample index outside the problem")
     return out
+
+
+def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, *, n_q: int, n_k: int, head_dim: int, scale: float,
+              batch: int = 1, ldq: int = 0, ldk: int = 0, ldv: int = 0, sq: int = 0, sk: int = 0, sv: int = 0,
+              in_dtype: str = "bf16", rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp64 reference of softmax(scale * Q K^T) V, no mask (oracle_attention.c).
+
+    Q, K, V are flat-addressable uint16 bit patterns, row-major with head_dim
+    contiguous.  Returns [len(rows), head_dim] for the requested (b, i) rows,
+    or [batch, n_q, head_dim] when ``rows`` is None.
+    """
+    lib = _load()
+    Q, K, V = _u16(Q), _u16(K), _u16(V)
+    ldq, ldk, ldv = ldq or head_dim, ldk or head_dim, ldv or head_dim
+    sq, sk, sv = sq or n_q * ldq, sk or n_k * ldk, sv or n_k * ldv
+    full = rows is None
+    if full:
+        bb, ii = np.meshgrid(np.arange(batch), np.arange(n_q), indexing="ij")
+        rows = np.stack([bb.ravel(), ii.ravel()], 1)
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 2)
+    out = np.empty((rows.shape[0], head_dim), dtype=np.float64)
+    rc = lib.oracle_attention(IN_TYPES[in_dtype], n_q, n_k, head_dim, float(scale), _ptr(Q), ldq, sq, _ptr(K), ldk,
+                              sk, _ptr(V), ldv, sv, batch, _ptr(rows), rows.shape[0], _ptr(out))
+    if rc != 0:
+        raise IndexError("oracle_attention: row outside the problem, n_k < 1, or out of memory")
+    return out.reshape(batch, n_q, head_dim) if full else out
 
 
 def gemm_problem(p, idx: Optional[np.ndarray] = None) -> np.ndarray:

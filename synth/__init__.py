@@ -174,6 +174,50 @@ def square_8192(seed: int = 4, out_dtype: str = "bf16") -> List[Problem]:
     return [Problem("square_8192_nn", A, B, 0, 0, 8192, 8192, 8192, out_dtype=out_dtype)]
 
 
+@dataclasses.dataclass
+class AttnProblem:
+    """O = softmax(scale * Q K^T) V for ``batch`` heads, row-major with the head
+    dimension contiguous: Q [batch, n_q, d], K and V [batch, n_k, d]."""
+    name: str
+    Q: np.ndarray
+    K: np.ndarray
+    V: np.ndarray
+    n_q: int
+    n_k: int
+    d: int
+    scale: float
+    batch: int = 1
+    out_dtype: str = "fp32"
+
+    @property
+    def flops(self) -> float:
+        """Two n_q x n_k x d products per head (the softmax's arithmetic is not counted)."""
+        return 4.0 * self.batch * self.n_q * self.n_k * self.d
+
+
+def attention_fwd(seed: int = 5, batch: int = 128, seq: int = 2048, head: int = 128,
+                  out_dtype: str = "fp32") -> AttnProblem:
+    """Fused attention forward pass on the attention-shaped workload's sizes:
+    Q, K, V ~ N(0, 1) drawn in that order from one stream, scale 1/sqrt(head)."""
+    rng = np.random.default_rng(seed)
+    Q = draw(rng, (batch, seq, head), "normal", 1.0)
+    K = draw(rng, (batch, seq, head), "normal", 1.0)
+    V = draw(rng, (batch, seq, head), "normal", 1.0)
+    return AttnProblem(f"attn_fwd_b{batch}_{seq}x{seq}_d{head}", Q, K, V, seq, seq, head, 1.0 / float(np.sqrt(head)),
+                       batch, out_dtype)
+
+
+def attention_rows(seed: int, batch: int, n_q: int, count: int = 512,
+                   edges: Tuple[int, ...] = (0, 31, 32, 63, 64, 127, 128)) -> np.ndarray:
+    """Seeded (b, i) query rows: ``count`` uniform draws plus tile-edge rows in
+    the first and last head."""
+    rng = np.random.default_rng(2000 + seed)
+    r = np.stack([rng.integers(0, batch, count), rng.integers(0, n_q, count)], 1)
+    e = [i for i in edges if i < n_q] + [n_q - 1]
+    extra = [[b, i] for b in {0, batch - 1} for i in e]
+    return np.concatenate([r, np.array(extra, dtype=np.int64)]).astype(np.int64)
+
+
 WORKLOADS = {
     "square_256": square_256,
     "ragged_1000": ragged_1000,

@@ -282,3 +282,109 @@ def test_max_abs_matches_decoded_maximum():
     rng = np.random.default_rng(20)
     X = rand_bf16(rng, (300, 301), 5.0)
     assert oracle.max_abs(X) == np.max(np.abs(oracle.decode(X)))
+
+
+# ----------------------------------------------------------------------------
+# fused attention forward: O = softmax(scale * Q K^T) V (no mask)
+# ----------------------------------------------------------------------------
+
+def _attn_inputs(seed, batch, n_q, n_k, d, dist=("normal", 1.0)):
+    rng = np.random.default_rng(seed)
+    Q = synth.draw(rng, (batch, n_q, d), *dist)
+    K = synth.draw(rng, (batch, n_k, d), *dist)
+    V = synth.draw(rng, (batch, n_k, d), *dist)
+    return Q, K, V
+
+
+def test_attention_identical_keys_give_the_mean_of_v():
+    """All scores of a row equal -> uniform weights -> O is the plain mean of V's rows."""
+    Q, K, V = _attn_inputs(11, 2, 3, 9, 8)
+    K[:] = K[:, :1, :]                       # every key is the first key
+    o = oracle.attention(Q, K, V, n_q=3, n_k=9, head_dim=8, scale=0.7, batch=2)
+    mean = oracle.decode(V).reshape(2, 9, 8).mean(axis=1)
+    np.testing.assert_allclose(o, np.broadcast_to(mean[:, None, :], o.shape), rtol=0, atol=1e-15)
+
+
+def test_attention_single_key_returns_that_value_row():
+    Q, K, V = _attn_inputs(12, 2, 4, 1, 16)
+    o = oracle.attention(Q, K, V, n_q=4, n_k=1, head_dim=16, scale=3.0, batch=2)
+    v = oracle.decode(V).reshape(2, 1, 16)
+    assert np.array_equal(o, np.broadcast_to(v, o.shape))
+
+
+def test_attention_dominant_key_selects_its_value_row():
+    """One key aligned with the query and a large scale: weight ~1 on it, < exp(-40) elsewhere."""
+    d, n_k = 8, 6
+    Q = np.zeros((1, 1, d), np.uint16)
+    K = np.zeros((1, n_k, d), np.uint16)
+    Q[0, 0, 0] = 0x3F80                      # q = e0 (bf16 1.0)
+    for j in range(n_k):
+        K[0, j, 0] = 0x3F80 if j == 4 else 0x3F00   # key 4 scores 1.0, the others 0.5
+    rng = np.random.default_rng(13)
+    V = synth.draw(rng, (1, n_k, d), "normal", 1.0)
+    o = oracle.attention(Q, K, V, n_q=1, n_k=n_k, head_dim=d, scale=100.0)
+    v = oracle.decode(V).reshape(n_k, d)
+    np.testing.assert_allclose(o[0, 0], v[4], rtol=0, atol=6 * np.exp(-50.0) * np.abs(v).max() + 1e-300)
+
+
+def test_attention_equals_gemm_then_numpy_softmax_then_numpy_matmul():
+    """The same definition composed from the pinned GEMM oracle, numpy's softmax
+    arithmetic and numpy's matmul."""
+    b, n_q, n_k, d = 3, 17, 33, 24
+    Q, K, V = _attn_inputs(14, b, n_q, n_k, d)
+    scale = 1.0 / np.sqrt(d)
+    o = oracle.attention(Q, K, V, n_q=n_q, n_k=n_k, head_dim=d, scale=scale, batch=b)
+    s = oracle.gemm(Q, K, m=n_q, n=n_k, k=d, trans_b=1, batch=b, stride_a=n_q * d, stride_b=n_k * d) * scale
+    w = np.exp(s - s.max(axis=2, keepdims=True))
+    p = w / w.sum(axis=2, keepdims=True)
+    ref = p @ oracle.decode(V).reshape(b, n_k, d)
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_tiny_brute_force_in_pure_python():
+    import math
+    n_q, n_k, d = 2, 5, 3
+    Q, K, V = _attn_inputs(15, 1, n_q, n_k, d)
+    q, k, v = (oracle.decode(x).reshape(-1, d).tolist() for x in (Q, K, V))
+    scale = 0.9
+    o = oracle.attention(Q, K, V, n_q=n_q, n_k=n_k, head_dim=d, scale=scale)
+    for i in range(n_q):
+        s = [scale * math.fsum(q[i][t] * k[j][t] for t in range(d)) for j in range(n_k)]
+        w = [math.exp(x) for x in s]        # small scores: no shift needed
+        den = math.fsum(w)
+        for c in range(d):
+            want = math.fsum(w[j] * v[j][c] for j in range(n_k)) / den
+            assert abs(o[0, i, c] - want) <= 1e-14 * max(1.0, abs(want))
+
+
+def test_attention_is_invariant_to_key_order_and_to_a_common_score_shift():
+    b, n_q, n_k, d = 2, 5, 12, 8
+    Q, K, V = _attn_inputs(16, b, n_q, n_k, d)
+    o = oracle.attention(Q, K, V, n_q=n_q, n_k=n_k, head_dim=d, scale=0.5, batch=b)
+    perm = np.random.default_rng(17).permutation(n_k)
+    o2 = oracle.attention(Q, K[:, perm], V[:, perm], n_q=n_q, n_k=n_k, head_dim=d, scale=0.5, batch=b)
+    np.testing.assert_allclose(o2, o, rtol=1e-13, atol=1e-13)
+    # one more feature column with q = 1 and k = 2 for every key adds 2*scale to every score
+    one, two = np.uint16(0x3F80), np.uint16(0x4000)
+    Qx = np.concatenate([Q, np.full((b, n_q, 1), one, np.uint16)], axis=2)
+    Kx = np.concatenate([K, np.full((b, n_k, 1), two, np.uint16)], axis=2)
+    Vx = np.concatenate([V, np.zeros((b, n_k, 1), np.uint16)], axis=2)
+    o3 = oracle.attention(Qx, Kx, Vx, n_q=n_q, n_k=n_k, head_dim=d + 1, scale=0.5, batch=b)
+    np.testing.assert_allclose(o3[:, :, :d], o, rtol=1e-13, atol=1e-13)
+
+
+def test_attention_rows_and_strides_address_the_right_data():
+    """Sampled rows equal the full result; padded leading dimensions and batch
+    strides only move where rows are read."""
+    b, n_q, n_k, d = 3, 7, 10, 8
+    Q, K, V = _attn_inputs(18, b, n_q, n_k, d)
+    full = oracle.attention(Q, K, V, n_q=n_q, n_k=n_k, head_dim=d, scale=0.3, batch=b)
+    rows = np.array([[0, 0], [2, 6], [1, 3], [2, 0]])
+    part = oracle.attention(Q, K, V, n_q=n_q, n_k=n_k, head_dim=d, scale=0.3, batch=b, rows=rows)
+    assert np.array_equal(part, full[rows[:, 0], rows[:, 1]])
+    pad = lambda X, ld: np.concatenate([X, np.full(X.shape[:2] + (ld - d,), np.uint16(0x7FC0))], axis=2)
+    got = oracle.attention(pad(Q, 11), pad(K, 9), pad(V, 13), n_q=n_q, n_k=n_k, head_dim=d, scale=0.3, batch=b,
+                           ldq=11, ldk=9, ldv=13)
+    assert np.array_equal(got, full)
+    with pytest.raises(IndexError):
+        oracle.attention(Q, K, V, n_q=n_q, n_k=n_k, head_dim=d, scale=0.3, batch=b, rows=np.array([[3, 0]]))
