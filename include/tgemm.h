@@ -154,6 +154,36 @@ tg_status gemm_run(const gemm_plan_t* plan, const void* A, const void* B, void* 
 tg_status bmm_run(const gemm_plan_t* plan, int64_t batch, int64_t stride_a, int64_t stride_b,
                   int64_t stride_c, const void* A, const void* B, void* C, hipStream_t stream);
 
+/*
+ * attention_fwd -- fused attention forward pass, enqueued on `stream`:
+ *     O[b] = softmax(scale * Q[b] K[b]^T) V[b]        b = 0 .. batch-1
+ * the attention-shaped pair of products the pages' GEMM/BMM/attention
+ * reference names as its companion target ("Triton Optimization Reference
+ * (cuTile -> Triton)", opening section), chained through a row softmax
+ * (over all n_k keys: no mask) inside one kernel, so the n_q x n_k scores
+ * and probabilities never reach memory.
+ *   Q[b] is n_q x head_dim, element (i,c) at Q + b*stride_q + i*ldq + c;
+ *   K[b] and V[b] are n_k x head_dim, likewise with ldk/stride_k, ldv/stride_v;
+ *   O[b] is n_q x head_dim at O + b*stride_o + i*ldo + c   (all in elements).
+ * in_type: TG_BF16 or TG_FP16 (Q, K, V alike); out_type: TG_FP32 or in_type.
+ * Scores and sums are fp32; the probabilities are rounded to in_type before
+ * the product with V (round to nearest even), and O to out_type.
+ * head_dim: 64 or 128.  scale: finite and > 0 (1/sqrt(head_dim) is the usual
+ * choice).  Leading dims >= head_dim, < 2^20, multiples of 8; the four base
+ * pointers 16-byte aligned and (batch > 1) the strides multiples of 8.
+ * Ownership: all pointers are caller-owned device memory; nothing is
+ * allocated.  O must not alias Q, K or V; heads' outputs must not overlap.
+ * Returns TG_OK (batch = 0 or n_q = 0 launches nothing), TG_ERR_INVALID
+ * (negative size or stride, n_k = 0 with work to do, bad scale, leading dim
+ * below head_dim, null pointer, overlapping outputs, offset overflow),
+ * TG_ERR_UNSUPPORTED (dtype pair, head_dim, alignment, leading dim >= 2^20),
+ * TG_ERR_HIP (launch failed).
+ */
+tg_status attention_fwd(tg_dtype in_type, tg_dtype out_type, int64_t batch, int64_t n_q, int64_t n_k,
+                        int64_t head_dim, float scale, const void* Q, int64_t ldq, int64_t stride_q,
+                        const void* K, int64_t ldk, int64_t stride_k, const void* V, int64_t ldv,
+                        int64_t stride_v, void* O, int64_t ldo, int64_t stride_o, hipStream_t stream);
+
 /* Static text for a status code ("ok", "invalid argument", ...). */
 const char* tg_status_str(tg_status s);
 

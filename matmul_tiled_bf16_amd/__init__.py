@@ -88,6 +88,9 @@ def lib() -> ctypes.CDLL:
                                i64, i64, i64, i64, i64, i64, i64]
         L.gemm_plan_tile.restype = ctypes.c_int
         L.gemm_plan_tile.argtypes = [ctypes.POINTER(GemmPlan), i32, i32]
+        L.attention_fwd.restype = ctypes.c_int
+        L.attention_fwd.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
+                                    p, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, p]
         if L.tg_abi_version() != _abi_version_from_header():
             raise RuntimeError("libtgemm.so was built from a different tgemm.h (ABI version mismatch)")
         _lib = L
@@ -218,4 +221,41 @@ def bmm(A, B, *, trans_a: bool = False, trans_b: bool = False, out_dtype=None, o
     p = plan(m, n, k, trans_a=trans_a, trans_b=trans_b, in_dtype=A.dtype, out_dtype=out_dtype, lda=_ld(A),
              ldb=_ld(B), ldc=_ld(out), batch=max(batch, 1))
     bmm_run(p, batch, A.stride(0), B.stride(0), out.stride(0), A, B, out, stream)
+    return out
+
+
+def attention_fwd(in_type: int, out_type: int, batch: int, n_q: int, n_k: int, head_dim: int, scale: float,
+                  Q, ldq: int, stride_q: int, K, ldk: int, stride_k: int, V, ldv: int, stride_v: int,
+                  O, ldo: int, stride_o: int, stream=None) -> None:
+    """attention_fwd(): raw call (dtype codes, pointers or tensors, element strides)."""
+    st = lib().attention_fwd(in_type, out_type, batch, n_q, n_k, head_dim, ctypes.c_float(scale), _ptr(Q), ldq,
+                             stride_q, _ptr(K), ldk, stride_k, _ptr(V), ldv, stride_v, _ptr(O), ldo, stride_o,
+                             _stream_handle(stream))
+    if st != TG_OK:
+        raise TgError(st, "attention_fwd")
+
+
+def attention(Q, K, V, *, scale: Optional[float] = None, out_dtype=None, out=None, stream=None):
+    """O = softmax(scale * Q K^T) V per head for 3-D tensors [batch, rows, head_dim]
+    (head_dim contiguous); scale defaults to 1/sqrt(head_dim).  Returns O (new, or ``out``)."""
+    import math
+    import torch
+    for X, name in ((Q, "Q"), (K, "K"), (V, "V")):
+        _check_matrix(X, name)
+        if X.dim() != 3:
+            raise ValueError(f"{name} must be 3-D [batch, rows, head_dim]")
+    if not (Q.dtype == K.dtype == V.dtype):
+        raise TypeError("Q, K and V must have the same dtype")
+    batch, n_q, d = Q.shape
+    if K.shape[0] != batch or V.shape[0] != batch or K.shape[2] != d or V.shape[2] != d or K.shape[1] != V.shape[1]:
+        raise ValueError("K and V must be [batch, n_k, head_dim] with Q's batch and head_dim")
+    n_k = K.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((batch, n_q, d), dtype=out_dtype, device=Q.device)
+    elif out.shape != (batch, n_q, d) or out.dtype != out_dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    attention_fwd(_dtype_code(Q.dtype), _dtype_code(out_dtype), batch, n_q, n_k, d, scale, Q, _ld(Q), Q.stride(0),
+                  K, _ld(K), K.stride(0), V, _ld(V), V.stride(0), out, _ld(out), out.stride(0), stream)
     return out

@@ -27,7 +27,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"gemm_plan", "bmm_plan", "gemm_plan_tile", "gemm_run", "bmm_run", "tg_status_str", "tg_abi_version",
-            "tg_variant_tiles"} <= set(names)
+            "tg_variant_tiles", "attention_fwd"} <= set(names)
     L = tg.lib()
     for n in names:
         assert hasattr(L, n), f"libtgemm.so does not export {n}"
@@ -220,6 +220,45 @@ def test_run_time_checks_that_need_no_gpu():
     assert L.gemm_run(ctypes.byref(e), None, None, None, None) == tg.TG_OK
     st, e = raw_plan(m=64, n=64, k=64)
     assert L.bmm_run(ctypes.byref(e), 0, 0, 0, 0, None, None, None, None) == tg.TG_OK
+
+
+def attn_call(**kw):
+    """attention_fwd with a valid 2 x 256 x 256 x 128 bf16 problem, overridden by kw."""
+    a = dict(in_type=tg.TG_BF16, out_type=tg.TG_FP32, batch=2, n_q=256, n_k=256, head_dim=128, scale=0.125,
+             Q=4096, ldq=128, sq=256 * 128, K=4096, ldk=128, sk=256 * 128, V=4096, ldv=128, sv=256 * 128,
+             O=4096, ldo=128, so=256 * 128)
+    a.update(kw)
+    return tg.lib().attention_fwd(a["in_type"], a["out_type"], a["batch"], a["n_q"], a["n_k"], a["head_dim"],
+                                  ctypes.c_float(a["scale"]), a["Q"], a["ldq"], a["sq"], a["K"], a["ldk"], a["sk"],
+                                  a["V"], a["ldv"], a["sv"], a["O"], a["ldo"], a["so"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), tg.TG_ERR_INVALID),
+    (dict(n_q=-1), tg.TG_ERR_INVALID),
+    (dict(n_k=0), tg.TG_ERR_INVALID),                  # softmax over no keys
+    (dict(scale=0.0), tg.TG_ERR_INVALID),
+    (dict(scale=-0.5), tg.TG_ERR_INVALID),
+    (dict(scale=float("inf")), tg.TG_ERR_INVALID),
+    (dict(scale=float("nan")), tg.TG_ERR_INVALID),
+    (dict(ldq=127), tg.TG_ERR_INVALID),
+    (dict(ldo=64), tg.TG_ERR_INVALID),
+    (dict(sk=-1), tg.TG_ERR_INVALID),
+    (dict(so=128), tg.TG_ERR_INVALID),                 # heads' outputs overlap
+    (dict(O=None), tg.TG_ERR_INVALID),
+    (dict(K=None), tg.TG_ERR_INVALID),
+    (dict(in_type=tg.TG_FP32), tg.TG_ERR_UNSUPPORTED),
+    (dict(in_type=tg.TG_FP16, out_type=tg.TG_BF16), tg.TG_ERR_UNSUPPORTED),
+    (dict(head_dim=96, ldq=128, ldk=128, ldv=128, ldo=128), tg.TG_ERR_UNSUPPORTED),
+    (dict(ldk=132), tg.TG_ERR_UNSUPPORTED),            # not a multiple of 8
+    (dict(V=4096 + 2), tg.TG_ERR_UNSUPPORTED),         # misaligned base
+    (dict(ldq=1 << 20, sq=256 << 20), tg.TG_ERR_UNSUPPORTED),
+    (dict(batch=0, Q=None, K=None, V=None, O=None), tg.TG_OK),   # nothing to do
+    (dict(n_q=0, n_k=0, O=None), tg.TG_OK),
+])
+def test_attention_argument_checks(kw, status):
+    """Every rejection (and the empty launches) happens before any device call."""
+    assert attn_call(**kw) == status
 
 
 def test_page_figures_pin_the_roofline_arithmetic():
