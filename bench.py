@@ -13,6 +13,8 @@ Workloads (seeded synthetic inputs from synth/):
   skinny_16     M=16, N=K=8192, B stored N x K, bf16 out  (HBM-bound)
   attention_s   128 x (2048x2048x128) S = Q K^T, fp32 out (HBM-bound)
   attention_o   128 x (2048x128x2048) O = P V,   fp32 out (HBM-bound)
+  attn_fwd      128 x fused softmax(Q K^T / sqrt(128)) V, 2048 x 2048, d = 128,
+                fp32 out (the same two products fused; MFMA-bound)
   ragged_1000   1000^3 NN, fp32 out
   square_256    256^3 NN, fp32 out
 
@@ -93,6 +95,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": profiling.COPY_BYTES, "copies": 4}))
         return
+
+    if args.workload == "attn_fwd":
+        return run_attention(args, torch, tg, profiling)
 
     (p,) = problems(args.workload)
     dev = torch.device("cuda:0")
@@ -195,6 +200,108 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(p, unit, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def run_attention(args, torch, tg, profiling):
+    """The fused attention forward pass: one step = one attention_fwd launch
+    over all heads.  Flops are the two products' 4 * batch * n_q * n_k * d
+    (the softmax's exponentials are not counted); algorithmic bytes are Q, K,
+    V read once and O written once."""
+    import synth
+    p = synth.attention_fwd()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tout = {"fp32": torch.float32, "bf16": torch.bfloat16}[p.out_dtype]
+    out_size = 4 if p.out_dtype == "fp32" else 2
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    Q, K, V = up(p.Q), up(p.K), up(p.V)
+    Os = [torch.empty((p.batch, p.n_q, p.d), dtype=tout, device=dev) for _ in range(2)]
+    stream = torch.cuda.current_stream()
+    flops = p.flops
+    nbytes = p.batch * (2 * p.n_q * p.d + 2 * 2 * p.n_k * p.d + out_size * p.n_q * p.d)
+    d = p.d
+
+    def step(i):
+        O = Os[i % 2]
+        tg.attention_fwd(tg.TG_BF16, tg.TG_FP32 if out_size == 4 else tg.TG_BF16, p.batch, p.n_q, p.n_k, d,
+                         p.scale, Q, d, p.n_q * d, K, d, p.n_k * d, V, d, p.n_k * d, O, d, p.n_q * d, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    assert torch.isfinite(Os[0].float()).all().item(), "non-finite output"
+    mean_ms, kms, queued_ahead = gated_kernel_ms(torch, stream, step, args.steps, max(args.warmup, 1))
+    kernel_s = mean_ms / 1e3
+    tflops = flops / (ms_per_step / 1e3) / 1e12
+    achieved = flops / kernel_s / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": p.name, "batch": p.batch, "n_q": p.n_q, "n_k": p.n_k, "head_dim": p.d,
+                   "scale": p.scale, "in_dtype": "bf16", "out_dtype": p.out_dtype, "fused": True},
+        "tflops": round(tflops, 2),
+        "pct_mfma_peak": round(100 * flops / (ms_per_step / 1e3) / PEAK_MFMA, 2),
+        "gbps": round(nbytes / (ms_per_step / 1e3) / 1e9, 1),
+        "pct_hbm_peak": round(100 * nbytes / (ms_per_step / 1e3) / PEAK_HBM, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA / 1e12,
+                     "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_MFMA, 4),
+                     "traffic": profiling.read_traffic(p.name),
+                     "kernel_ms": round(kernel_s * 1e3, 5),
+                     "kernel_ms_each_min": round(float(np.min(kms)), 5),
+                     "kernel_ms_each_p90": round(float(np.percentile(kms, 90)), 5),
+                     "launches_queued_ahead": bool(queued_ahead),
+                     "algorithmic": {"flops": flops, "bytes": nbytes}},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_attention(p, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_attention(p, seconds):
+    """Time the CPU oracle on seeded query rows of the attention workload."""
+    import oracle
+    import synth
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    kw = dict(n_q=p.n_q, n_k=p.n_k, head_dim=p.d, scale=p.scale, batch=p.batch)
+    count, dt = 8, 0.0
+    while True:
+        rows = synth.attention_rows(77, p.batch, p.n_q, count=count, edges=())
+        t0 = time.perf_counter()
+        oracle.attention(p.Q, p.K, p.V, rows=rows, **kw)
+        dt = max(time.perf_counter() - t0, 1e-4)
+        if dt >= 0.5 or count >= p.batch * p.n_q:
+            break
+        count = min(p.batch * p.n_q, count * 8)
+    count = int(max(8, min(p.batch * p.n_q, count * seconds / dt)))
+    rows = synth.attention_rows(78, p.batch, p.n_q, count=count, edges=())
+    t0 = time.perf_counter()
+    oracle.attention(p.Q, p.K, p.V, rows=rows, **kw)
+    t = time.perf_counter() - t0
+    flops = 4.0 * p.n_k * p.d * len(rows)
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} seeded query rows of the same workload (each {p.n_k} fp64 scores of "
+                      f"{p.d} terms, softmax, and a {p.n_k}-term weighted sum per output), {t:.1f} s on "
+                      f"{threads} threads; all {p.batch * p.n_q} rows would take "
+                      f"{t * p.batch * p.n_q / len(rows):.0f} s"}
 
 
 def _held(torch, stream, enqueue):

@@ -13,13 +13,13 @@ namespace {
 using tg::AttnArgs;
 using tg::AttnFn;
 
-// One launch shape per head dimension: 4 waves (128 query rows), 64 keys per
+// One launch shape per head dimension: 4 waves of 32 query rows, 64 keys per
 // stage, 2 stages (64 KiB of LDS at d = 128, so two work-groups share a CU).
-constexpr int kWaves = 4, kBN = 64, kStages = 2;
+constexpr int kWaves = 4, kRB = 1, kBN = 64, kStages = 2;
 
 template <typename In, typename Out, int D>
 constexpr AttnFn attn_kernel() {
-  return tg::attn_fwd_kernel<In, Out, D, kWaves, kBN, kStages>;
+  return tg::attn_fwd_kernel<In, Out, D, kWaves, kRB, kBN, kStages>;
 }
 
 // [in bf16/fp16][out fp32/same][d 64/128]
@@ -66,7 +66,7 @@ tg_status attention_fwd(tg_dtype in_type, tg_dtype out_type, int64_t batch, int6
                                        stride_o % 8 == 0));
   if (!aligned) return TG_ERR_UNSUPPORTED;
 
-  constexpr int BM = 32 * kWaves;
+  constexpr int BM = 32 * kRB * kWaves;
   const int64_t q_blocks = (n_q + BM - 1) / BM;
   if (q_blocks >= ((int64_t)1 << 31)) return TG_ERR_INVALID;
   const int64_t total = q_blocks * batch;

@@ -58,16 +58,19 @@ struct AttnArgs {
 
 using AttnFn = void (*)(AttnArgs);
 
-// D: head dimension; WAVES: waves per work-group (32 query rows each); BN:
-// keys per stage; S: LDS stages.
-// Two waves per SIMD: the softmax arithmetic of one wave overlaps the MFMAs of
-// the other.
-template <typename In, typename Out, int D, int WAVES, int BN, int S>
-__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
+// D: head dimension; WAVES: waves per work-group; RB: 32-row query blocks per
+// wave (each K or V fragment read from LDS feeds RB MFMAs); BN: keys per
+// stage; S: LDS stages.  RB = 1 runs two waves per SIMD (the softmax of one
+// overlaps the MFMAs of the other); RB = 2 needs the whole register file
+// (O alone is 128 registers per lane) and runs one.
+template <typename In, typename Out, int D, int WAVES, int RB, int BN, int S>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1)))
 attn_fwd_kernel(AttnArgs a) {
   static_assert(D == 64 || D == 128, "head dimension 64 or 128");
+  static_assert(RB == 1 || RB == 2, "one or two row blocks per wave");
   static_assert(BN % 32 == 0 && S >= 2 && S <= 4, "stage shape");
-  constexpr int BM = 32 * WAVES;
+  constexpr int WR = 32 * RB;            // query rows per wave
+  constexpr int BM = WR * WAVES;         // query rows per work-group
   constexpr int ROWB = 2 * D;            // bytes of one K or V row
   constexpr int DCH = D / 8;             // 16-byte units per row
   constexpr int TI = BN * ROWB / 1024;   // 1 KiB wave copies per K (or V) tile
@@ -126,29 +129,36 @@ attn_fwd_kernel(AttnArgs a) {
       for (int i = 0; i < PW; ++i) dma16(rv, voff[i], st + TILE + (uint32_t)i * 1024u);
     };
 
-    // Q fragments of this lane's row: d = 16 ks + 8 lg .. +7
-    u32x4 qf[DS];
+    // Q fragments of this lane's rows: row block rb, d = 16 ks + 8 lg .. +7
+    u32x4 qf[RB][DS];
     {
       const __amdgpu_buffer_rsrc_t rq =
           store_rsrc(a.Q + b * a.sq + q0 * a.ldq, ((rows_q - 1) * a.ldq + D) * 2);
-      const uint32_t ro = (uint32_t)((wave * 32 + li) * a.ldq * 2);
 #pragma unroll
-      for (int ks = 0; ks < DS; ++ks)
-        qf[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rq, (int)(ro + (uint32_t)(16 * ks + 8 * lg) * 2), 0, 0));
+      for (int rb = 0; rb < RB; ++rb) {
+        const uint32_t ro = (uint32_t)((wave * WR + rb * 32 + li) * a.ldq * 2);
+#pragma unroll
+        for (int ks = 0; ks < DS; ++ks)
+          qf[rb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rq, (int)(ro + (uint32_t)(16 * ks + 8 * lg) * 2), 0, 0));
+      }
     }
 
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
       if (s < nkb) issue(s, s);
 
-    f32x16 o[DB];
+    f32x16 o[RB][DB];
+    float m[RB], l[RB];
 #pragma unroll
-    for (int i = 0; i < DB; ++i)
+    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
-    float m = -__builtin_inff();  // running maximum, log2 units
-    float l = 0.f;                // this lane's share of the row sum
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[rb][i][r] = 0.f;
+      m[rb] = -__builtin_inff();  // running maximum, log2 units
+      l[rb] = 0.f;                // this lane's share of the row sum
+    }
 
     for (int64_t j = 0; j < nkb; ++j) {
       // own copies of block j have landed (later blocks may still be in
@@ -159,64 +169,32 @@ attn_fwd_kernel(AttnArgs a) {
       const TG_LDS char* kt = lds + (uint32_t)(j % S) * STAGE;
       const TG_LDS char* vt = kt + TILE;
 
-      // scores S^T for BN keys x 32 query rows
-      f32x16 sc[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+      // K fragments of the whole stage, all in flight before the first MFMA
+      u32x4 kf[DS][NKB];
 #pragma unroll
       for (int ks = 0; ks < DS; ++ks)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const u32x4 kf = lds_read16(kt, swz_off<true, DCH>(kb * 32 + li, ks * 16 + lg * 8));
-          sc[kb] = mfma32<In>(kf, qf[ks], sc[kb]);
-        }
+        for (int kb = 0; kb < NKB; ++kb)
+          kf[ks][kb] = lds_read16(kt, swz_off<true, DCH>(kb * 32 + li, ks * 16 + lg * 8));
 
-      // keys past n_k (last block only) take no weight
-      const int64_t valid = a.n_k - j * BN;
-      if (valid < BN) {
+      // scores S^T for BN keys x 32 query rows, per row block
+      f32x16 sc[RB][NKB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kb * 32 + 8 * (r >> 2) + 4 * lg + (r & 3) >= valid) sc[kb][r] = -__builtin_inff();
-      }
+          for (int r = 0; r < 16; ++r) sc[rb][kb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < DS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) sc[rb][kb] = mfma32<In>(kf[ks][kb], qf[rb][ks], sc[rb][kb]);
 
-      // row maximum over this block (both lane halves)
-      float mx = sc[0][0];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mxs = mx * a.c;
-      if (__builtin_amdgcn_ballot_w64(mxs > m + TAU)) {
-        const float mn = fmaxf(m, mxs);
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        m = mn;
-        l *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      }
-
-      // probabilities (unnormalised), their row sum, and P V
-      u32x4 pf[KS];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], a.c, -m));
-          l += p[r];
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          pf[2 * kb + h] = u32x4{pack2<In>(p[8 * h], p[8 * h + 1]), pack2<In>(p[8 * h + 2], p[8 * h + 3]),
-                                 pack2<In>(p[8 * h + 4], p[8 * h + 5]), pack2<In>(p[8 * h + 6], p[8 * h + 7])};
-      }
+      // V fragments, in flight while the softmax runs: lane half lg supplies
+      // keys 16t + 4lg + {0..3} and 16t + 8 + 4lg + {0..3} of step t
+      u32x4 vf[KS][DB];
 #pragma unroll
       for (int t = 0; t < KS; ++t)
 #pragma unroll
@@ -225,28 +203,96 @@ attn_fwd_kernel(AttnArgs a) {
           const int kr = t * 16 + 4 * lg + (trs >> 2);
           const u32x2 lo = lds_read_tr(vt, swz_off<false, DCH>(kr, col));
           const u32x2 hi = lds_read_tr(vt, swz_off<false, DCH>(kr + 8, col));
-          o[db] = mfma32<In>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[t], o[db]);
+          vf[t][db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // keys past n_k (last block only) take no weight; lane half lg holds
+      // key kb*32 + 8(r>>2) + 4lg + (r&3) in register r
+      const int valid = (int)min((int64_t)BN, a.n_k - j * BN);
+      if (valid < BN) {
+        const int thr = valid - 4 * lg;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (kb * 32 + 8 * (r >> 2) + (r & 3) >= thr) sc[rb][kb][r] = -__builtin_inff();
+      }
+
+      u32x4 pf[RB][KS];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        // row maximum over this block (both lane halves)
+        float mx = sc[rb][0][0];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[rb][kb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mxs = mx * a.c;
+        if (__builtin_amdgcn_ballot_w64(mxs > m[rb] + TAU)) {
+          const float mn = fmaxf(m[rb], mxs);
+          const float alpha = __builtin_amdgcn_exp2f(m[rb] - mn);
+          m[rb] = mn;
+          l[rb] *= alpha;
+#pragma unroll
+          for (int i = 0; i < DB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[rb][i][r] *= alpha;
+        }
+        // probabilities (unnormalised) and their row sum (four partial sums)
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          float p[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rb][kb][r], a.c, -m[rb]));
+            ls[r & 3] += p[r];
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            pf[rb][2 * kb + h] =
+                u32x4{pack2<In>(p[8 * h], p[8 * h + 1]), pack2<In>(p[8 * h + 2], p[8 * h + 3]),
+                      pack2<In>(p[8 * h + 4], p[8 * h + 5]), pack2<In>(p[8 * h + 6], p[8 * h + 7])};
+        }
+        l[rb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // O += P V
+#pragma unroll
+      for (int t = 0; t < KS; ++t)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma32<In>(vf[t][db], pf[rb][t], o[rb][db]);
     }
 
-    // normalise and store: register r of block db is O[row li][db*32 + 8(r>>2) + 4 lg + (r&3)]
-    l += __shfl_xor(l, 32);
-    const float inv = 1.f / l;
+    // normalise and store: register r of o[rb][db] is
+    // O[row rb*32 + li][db*32 + 8(r>>2) + 4 lg + (r&3)]
     Out* Oh = (Out*)a.O + b * a.so + q0 * a.ldo;
     const __amdgpu_buffer_rsrc_t ro = store_rsrc(Oh, ((rows_q - 1) * a.ldo + D) * (int64_t)sizeof(Out));
-    const uint32_t rowoff = (uint32_t)((wave * 32 + li) * a.ldo * (int64_t)sizeof(Out));
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int rb = 0; rb < RB; ++rb) {
+      const float lt = l[rb] + __shfl_xor(l[rb], 32);
+      const float inv = 1.f / lt;
+      const uint32_t rowoff = (uint32_t)((wave * WR + rb * 32 + li) * a.ldo * (int64_t)sizeof(Out));
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t off = rowoff + (uint32_t)(db * 32 + 8 * g + 4 * lg) * (uint32_t)sizeof(Out);
-        const float v0 = o[db][4 * g] * inv, v1 = o[db][4 * g + 1] * inv;
-        const float v2 = o[db][4 * g + 2] * inv, v3 = o[db][4 * g + 3] * inv;
-        if constexpr (sizeof(Out) == 4)
-          buf_store16(ro, off, __builtin_bit_cast(u32x4, f32x4{v0, v1, v2, v3}));
-        else
-          buf_store8(ro, off, u32x2{pack2<Out>(v0, v1), pack2<Out>(v2, v3)});
-      }
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t off = rowoff + (uint32_t)(db * 32 + 8 * g + 4 * lg) * (uint32_t)sizeof(Out);
+          const float v0 = o[rb][db][4 * g] * inv, v1 = o[rb][db][4 * g + 1] * inv;
+          const float v2 = o[rb][db][4 * g + 2] * inv, v3 = o[rb][db][4 * g + 3] * inv;
+          if constexpr (sizeof(Out) == 4)
+            buf_store16(ro, off, __builtin_bit_cast(u32x4, f32x4{v0, v1, v2, v3}));
+          else
+            buf_store8(ro, off, u32x2{pack2<Out>(v0, v1), pack2<Out>(v2, v3)});
+        }
+    }
 
     // every wave is done with the ring before the next item refills it
     if (w0 + gridDim.x < total) {

@@ -9,14 +9,14 @@
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/cfetch -o run -- python bench.py --copy-calibration
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/cwrite -o run -- python bench.py --copy-calibration
 
-    python -m matmul_tiled_bf16_amd.profiling stats OUT/trace > profiles/<kernel>_<workload>_stats.txt
+    python -m matmul_tiled_bf16_amd.profiling stats OUT/trace [gemm|attention] > profiles/<kernel>_<workload>_stats.txt
     python -m matmul_tiled_bf16_amd.profiling traffic OUT <workload> > profiles/<workload>_traffic.txt
 
 FETCH_SIZE / WRITE_SIZE are reported in KiB per dispatch; the copy kernel
 moves a known number of bytes, and the ratio of that number to what the
-counter reads for it scales the GEMM kernel's reading to bytes.  A traffic
-file records a hash of the kernel sources; bench.py reports traffic only
-while the sources still match.
+counter reads for it scales the kernel's reading to bytes.  A traffic file
+records a hash of the sources its kernel family (GEMM or attention) is built
+from; bench.py reports traffic only while those sources still match.
 """
 from __future__ import annotations
 
@@ -30,12 +30,27 @@ from collections import defaultdict
 HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30  # bytes read and written by one calibration copy
 
-KERNEL_PATTERNS = ("tile_gemm_kernel", "skinny_gemm_kernel", "generic_gemm_kernel")
+# kernel families: the kernels' name patterns and the sources they are built from
+FAMILIES = {
+    "gemm": (("tile_gemm_kernel", "skinny_gemm_kernel", "generic_gemm_kernel"),
+             lambda f: not os.path.basename(f).startswith("attention")),
+    "attention": (("attn_fwd_kernel",),
+                  lambda f: os.path.basename(f) in ("attention.hpp", "attention.hip", "tile_gemm.hpp",
+                                                    "common.hpp")),
+}
 
 
-def source_hash() -> str:
+def family_of(workload: str) -> str:
+    return "attention" if workload.startswith("attn_fwd") else "gemm"
+
+
+def source_hash(family: str = "gemm") -> str:
+    """Hash of the sources the family's kernels are built from."""
+    keep = FAMILIES[family][1]
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
+        if not keep(f):
+            continue
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
             h.update(fh.read())
@@ -54,9 +69,9 @@ def _short(name: str) -> str:
     return name if len(name) <= 110 else name[:107] + "..."
 
 
-def stats(trace_dir: str) -> str:
+def stats(trace_dir: str, family: str = "gemm") -> str:
     rows = _csv(trace_dir, "kernel_stats.csv")
-    out = [f"# rocprofv3 --kernel-trace --stats summary  (source hash {source_hash()})",
+    out = [f"# rocprofv3 --kernel-trace --stats summary  ({family} source hash {source_hash(family)})",
            f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_%':>8}  kernel"]
     for r in rows:
         avg = float(r["AverageNs"]) / 1e3
@@ -76,7 +91,8 @@ def _per_dispatch(path_dir: str, counter: str, match) -> list:
 
 
 def traffic(out_dir: str, workload: str) -> str:
-    is_ours = lambda n: any(p in n for p in KERNEL_PATTERNS)
+    family = family_of(workload)
+    is_ours = lambda n: any(p in n for p in FAMILIES[family][0])
     is_copy = lambda n: "copy" in n.lower() and not is_ours(n)
     f = _per_dispatch(os.path.join(out_dir, "fetch"), "FETCH_SIZE", is_ours)
     w = _per_dispatch(os.path.join(out_dir, "write"), "WRITE_SIZE", is_ours)
@@ -89,8 +105,8 @@ def traffic(out_dir: str, workload: str) -> str:
     fetch = mean(f) * kf
     write = mean(w) * kw
     lines = [
-        f"# HBM traffic per launch of the GEMM kernel, workload {workload}",
-        f"source_hash = {source_hash()}",
+        f"# HBM traffic per launch of the {family} kernel, workload {workload}",
+        f"source_hash = {source_hash(family)}",
         f"dispatches_fetch = {len(f)}",
         f"dispatches_write = {len(w)}",
         f"fetch_kib_counter = {mean(f):.1f}",
@@ -118,18 +134,18 @@ def read_traffic(workload: str):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("source_hash") != source_hash():
+    if kv.get("source_hash") != source_hash(family_of(workload)):
         return None
     return float(kv["traffic_bytes"])
 
 
 def main(argv):
     if argv[0] == "stats":
-        print(stats(argv[1]))
+        print(stats(argv[1], argv[2] if len(argv) > 2 else "gemm"))
     elif argv[0] == "traffic":
         print(traffic(argv[1], argv[2]))
     elif argv[0] == "hash":
-        print(source_hash())
+        print(source_hash(argv[1] if len(argv) > 1 else "gemm"))
     else:
         raise SystemExit(__doc__)
 
