@@ -15,6 +15,8 @@ Workloads (seeded synthetic inputs from synth/):
   attention_o   128 x (2048x128x2048) O = P V,   fp32 out (HBM-bound)
   attn_fwd      128 x fused softmax(Q K^T / sqrt(128)) V, 2048 x 2048, d = 128,
                 fp32 out (the same two products fused; MFMA-bound)
+  group_moe     32 ragged expert GEMMs (8192 tokens, K = N = 1024, NN, bf16 out)
+                in one grouped launch; also times one launch per problem
   ragged_1000   1000^3 NN, fp32 out
   square_256    256^3 NN, fp32 out
 
@@ -72,6 +74,7 @@ def main():
     ap.add_argument("--no-persist", action="store_true", help="clear the plan's persistent-launch flags")
     ap.add_argument("--no-prefetch", action="store_true", help="clear the plan's prefetch flag")
     ap.add_argument("--prefetch", action="store_true", help="set the plan's persistent and prefetch flags")
+    ap.add_argument("--group-tile", type=int, default=-1, help="force the grouped launch's tile (group_moe)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to calibrate FETCH_SIZE/WRITE_SIZE)")
@@ -98,6 +101,8 @@ def main():
 
     if args.workload == "attn_fwd":
         return run_attention(args, torch, tg, profiling)
+    if args.workload == "group_moe":
+        return run_group(args, torch, tg, profiling)
 
     (p,) = problems(args.workload)
     dev = torch.device("cuda:0")
@@ -274,6 +279,142 @@ def run_attention(args, torch, tg, profiling):
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_attention(p, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def run_group(args, torch, tg, profiling):
+    """Grouped launch: one step = one gemm_group_run over every expert's
+    product.  Algorithmic bytes are the tokens and the weights read once and
+    the outputs written once; the group is HBM-bound when their ratio to the
+    flops is below MI355X's ridge.  The same products launched one by one
+    (gemm_plan + gemm_run each) are timed the same way for comparison."""
+    import ctypes
+    import synth
+    p = synth.grouped_moe()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X, W = up(p.X), up(p.W)
+    T = int(p.counts.sum())
+    Ys = [torch.empty((T, p.n), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    off = p.offsets
+    es = 2
+    tables = []
+    for Y in Ys:
+        arr = (tg.GroupProblem * len(p.counts))()
+        for e, c in enumerate(p.counts):
+            arr[e] = tg.GroupProblem(int(c), p.n, p.k, p.k, p.n, p.n, X.data_ptr() + es * int(off[e]) * p.k,
+                                     W[e].data_ptr(), Y.data_ptr() + es * int(off[e]) * p.n)
+        tables.append(arr)
+    L = tg.lib()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    count = len(p.counts)
+
+    def step(i):
+        st = L.gemm_group_run(tg.TG_BF16, tg.TG_BF16, 0, 0, tables[i % 2], count, args.group_tile, sh)
+        if st != tg.TG_OK:
+            raise tg.TgError(st, "gemm_group_run")
+
+    def step_separate(i):
+        Y = Ys[i % 2]
+        for e, c in enumerate(p.counts):
+            if c == 0:
+                continue
+            pl = tg.plan(int(c), p.n, p.k, in_dtype=torch.bfloat16, out_dtype=torch.bfloat16)
+            tg.gemm_run(pl, X[int(off[e]):int(off[e + 1])], W[e], Y[int(off[e]):int(off[e + 1])], stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    assert torch.isfinite(Ys[0].float()).all().item(), "non-finite output"
+    mean_ms, kms, queued_ahead = gated_kernel_ms(torch, stream, step, args.steps, max(args.warmup, 1))
+    sep_ms, _, sep_ahead = gated_kernel_ms(torch, stream, step_separate, max(args.steps // 4, 3), 2)
+    flops = p.flops
+    nbytes = p.algorithmic_bytes(es)
+    bound = "mfma" if flops / nbytes > PEAK_MFMA / PEAK_HBM else "hbm"
+    kernel_s = mean_ms / 1e3
+    if bound == "mfma":
+        achieved, peak, runit = flops / kernel_s / 1e12, PEAK_MFMA / 1e12, "TFLOP/s"
+    else:
+        achieved, peak, runit = nbytes / kernel_s / 1e9, PEAK_HBM / 1e9, "GB/s"
+    tflops = flops / (ms_per_step / 1e3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": p.name, "problems": count, "tokens": T, "n": p.n, "k": p.k, "op": "NN",
+                   "group_tile": args.group_tile,
+                   "in_dtype": "bf16", "out_dtype": p.out_dtype, "empty_problems": int((p.counts == 0).sum()),
+                   "max_m": int(p.counts.max()), "min_m": int(p.counts.min())},
+        "tflops": round(tflops, 2),
+        "pct_mfma_peak": round(100 * flops / (ms_per_step / 1e3) / PEAK_MFMA, 2),
+        "gbps": round(nbytes / (ms_per_step / 1e3) / 1e9, 1),
+        "pct_hbm_peak": round(100 * nbytes / (ms_per_step / 1e3) / PEAK_HBM, 2),
+        "separate_launches": {"kernel_ms": round(sep_ms, 5), "launches": int((p.counts > 0).sum()),
+                              "queued_ahead": bool(sep_ahead),
+                              "grouped_speedup": round(sep_ms / mean_ms, 3)},
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": runit,
+                     "frac": round(achieved / peak, 4), "traffic": profiling.read_traffic(p.name),
+                     "kernel_ms": round(kernel_s * 1e3, 5),
+                     "kernel_ms_each_min": round(float(np.min(kms)), 5),
+                     "kernel_ms_each_p90": round(float(np.percentile(kms, 90)), 5),
+                     "launches_queued_ahead": bool(queued_ahead),
+                     "algorithmic": {"flops": flops, "bytes": nbytes}},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_group(p, "TFLOP/s", args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_group(p, unit, seconds):
+    """Time the CPU oracle on seeded output elements spread over all experts."""
+    import oracle
+    import synth
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    off = p.offsets
+    T = int(off[-1])
+
+    def run(count, seed):
+        tri = synth.sample_indices(seed, 1, T, p.n, count=count, edges=())
+        e_of = np.searchsorted(off, tri[:, 1], side="right") - 1
+        t0 = time.perf_counter()
+        for e in np.unique(e_of):
+            sel = tri[e_of == e].copy()
+            sel[:, 1] -= off[e]
+            rows = p.X[int(off[e]):int(off[e + 1])]
+            oracle.gemm(rows, p.W[e], m=int(p.counts[e]), n=p.n, k=p.k, idx=sel)
+        return time.perf_counter() - t0, len(tri)
+
+    count, dt = 4096, 0.0
+    while True:
+        dt, _ = run(count, 77)
+        if dt >= 0.5 or count >= 50_000_000:
+            break
+        count = min(50_000_000, count * 8)
+    count = int(max(256, min(50_000_000, count * seconds / max(dt, 1e-4))))
+    t, got = run(count, 78)
+    flops = 2.0 * p.k * got
+    return {"value": round(flops / t / 1e12, 6), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{got} seeded output elements spread over the experts (each a {p.k}-term fp64 dot "
+                      f"product), {t:.1f} s on {threads} threads; all {T * p.n} would take "
+                      f"{t * T * p.n / got:.0f} s"}
 
 
 def cpu_baseline_attention(p, seconds):

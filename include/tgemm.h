@@ -155,6 +155,45 @@ tg_status bmm_run(const gemm_plan_t* plan, int64_t batch, int64_t stride_a, int6
                   int64_t stride_c, const void* A, const void* B, void* C, hipStream_t stream);
 
 /*
+ * gemm_group_run -- many independent products of different shapes in as few
+ * launches as possible: C_i = op(A_i) op(B_i), i = 0 .. count-1, all with the
+ * same types and transposes.  It applies the pages' batched-launch idea
+ * ("Triton Optimization Reference", section 8: several tensors per launch,
+ * with the host grouping them, to pay the launch overhead once) to GEMM
+ * lists: up to TG_GROUP_MAX problems share one grid, each work-group looking
+ * its problem up in a table passed with the launch arguments.
+ *   problems: caller-owned host array of `count` >= 0 descriptors (read
+ *     during the call only); each descriptor's sizes and leading dimensions
+ *     follow the storage table above; A, B, C are device pointers.
+ *   tile: -1 lets the library choose one tile shape per launch from the
+ *     group's totals; 0 .. tg_group_tiles()-1 forces one (tests, tuning).
+ * Problems with m = 0 or n = 0 are skipped; k = 0 writes zeros.  Problems the
+ * 16-byte vector loader cannot serve (misaligned base, leading dim or
+ * contiguous extent not a multiple of 8) run one by one through the
+ * element-wise loader.  Every problem is validated before anything is
+ * enqueued.  C_i must not alias any A_j, B_j or another C_j.  The library
+ * allocates nothing.  Returns TG_OK, TG_ERR_INVALID (count < 0, null array,
+ * an invalid problem as gemm_plan defines it, a null pointer with nonzero
+ * extents, more than 2^30 tiles in a problem), TG_ERR_UNSUPPORTED (dtype
+ * pair, tile out of range), TG_ERR_HIP.
+ */
+#define TG_GROUP_MAX 32
+
+typedef struct {
+  int64_t m, n, k;
+  int64_t lda, ldb, ldc;
+  const void* A;
+  const void* B;
+  void* C;
+} gemm_group_problem_t;
+
+tg_status gemm_group_run(tg_dtype in_type, tg_dtype out_type, int trans_a, int trans_b,
+                         const gemm_group_problem_t* problems, int64_t count, int32_t tile, hipStream_t stream);
+
+/* Number of tile shapes a grouped launch can be forced to (gemm_group_run's `tile`). */
+int32_t tg_group_tiles(void);
+
+/*
  * attention_fwd -- fused attention forward pass, enqueued on `stream`:
  *     O[b] = softmax(scale * Q[b] K[b]^T) V[b]        b = 0 .. batch-1
  * the attention-shaped pair of products the pages' GEMM/BMM/attention

@@ -53,6 +53,13 @@ class GemmPlan(ctypes.Structure):
                                          if n != "reserved0") + ")")
 
 
+class GroupProblem(ctypes.Structure):
+    """Mirror of gemm_group_problem_t."""
+    _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldc", ctypes.c_int64),
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p)]
+
+
 class TgError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__(f"{what}: {status_str(status)} (status {status})")
@@ -88,6 +95,11 @@ def lib() -> ctypes.CDLL:
                                i64, i64, i64, i64, i64, i64, i64]
         L.gemm_plan_tile.restype = ctypes.c_int
         L.gemm_plan_tile.argtypes = [ctypes.POINTER(GemmPlan), i32, i32]
+        L.gemm_group_run.restype = ctypes.c_int
+        L.gemm_group_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.POINTER(GroupProblem), i64, i32, p]
+        L.tg_group_tiles.restype = i32
+        L.tg_group_tiles.argtypes = []
         L.attention_fwd.restype = ctypes.c_int
         L.attention_fwd.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
                                     p, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, p]
@@ -259,3 +271,53 @@ def attention(Q, K, V, *, scale: Optional[float] = None, out_dtype=None, out=Non
     attention_fwd(_dtype_code(Q.dtype), _dtype_code(out_dtype), batch, n_q, n_k, d, scale, Q, _ld(Q), Q.stride(0),
                   K, _ld(K), K.stride(0), V, _ld(V), V.stride(0), out, _ld(out), out.stride(0), stream)
     return out
+
+
+def group_tiles() -> int:
+    """Tile shapes a grouped launch can be forced to (valid `tile` values of gemm_group_run)."""
+    return int(lib().tg_group_tiles())
+
+
+def gemm_group_run(in_type: int, out_type: int, trans_a: bool, trans_b: bool, problems, tile: int = -1,
+                   stream=None) -> None:
+    """gemm_group_run(): `problems` is a sequence of GroupProblem (or of 9-tuples
+    m, n, k, lda, ldb, ldc, A, B, C with tensors or raw pointers)."""
+    arr = (GroupProblem * max(len(problems), 1))()
+    for i, q in enumerate(problems):
+        if isinstance(q, GroupProblem):
+            arr[i] = q
+        else:
+            m, n, k, lda, ldb, ldc, A, B, C = q
+            arr[i] = GroupProblem(m, n, k, lda, ldb, ldc, _ptr(A) if A is not None else None,
+                                  _ptr(B) if B is not None else None, _ptr(C) if C is not None else None)
+    st = lib().gemm_group_run(in_type, out_type, int(trans_a), int(trans_b), arr, len(problems), tile,
+                              _stream_handle(stream))
+    if st != TG_OK:
+        raise TgError(st, "gemm_group_run")
+
+
+def gemm_group(As, Bs, *, trans_a: bool = False, trans_b: bool = False, out_dtype=None, outs=None, tile: int = -1,
+               stream=None):
+    """[op(A_i) @ op(B_i)] for lists of 2-D tensors of one dtype, in grouped launches; returns the outputs."""
+    import torch
+    if len(As) != len(Bs):
+        raise ValueError("As and Bs differ in length")
+    out_dtype = out_dtype or torch.float32
+    probs, res = [], []
+    for i, (A, B) in enumerate(zip(As, Bs)):
+        _check_matrix(A, "A")
+        _check_matrix(B, "B")
+        if A.dtype != As[0].dtype or B.dtype != As[0].dtype:
+            raise TypeError("all operands must have the same dtype")
+        m, k = (A.shape[1], A.shape[0]) if trans_a else (A.shape[0], A.shape[1])
+        kb, n = (B.shape[1], B.shape[0]) if trans_b else (B.shape[0], B.shape[1])
+        if kb != k:
+            raise ValueError(f"problem {i}: inner dimensions differ: {k} vs {kb}")
+        C = outs[i] if outs is not None else torch.empty((m, n), dtype=out_dtype, device=A.device)
+        if C.shape != (m, n) or C.dtype != out_dtype:
+            raise ValueError(f"problem {i}: output has the wrong shape or dtype")
+        probs.append((m, n, k, _ld(A), _ld(B), _ld(C), A, B, C))
+        res.append(C)
+    if probs:
+        gemm_group_run(_dtype_code(As[0].dtype), _dtype_code(out_dtype), trans_a, trans_b, probs, tile, stream)
+    return res

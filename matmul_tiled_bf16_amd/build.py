@@ -42,7 +42,8 @@ def _units():
             for tb in (0, 1):
                 tag = f"{i}_{o}_{ta}{tb}"
                 defs = [f"-DTG_IN={TYPES[i]}", f"-DTG_OUT={TYPES[o]}", f"-DTG_TA={ta}", f"-DTG_TB={tb}",
-                        f"-DTG_TABLE_TILE=tile_{tag}", f"-DTG_TABLE_GENERIC=generic_{tag}"]
+                        f"-DTG_TABLE_TILE=tile_{tag}", f"-DTG_TABLE_GENERIC=generic_{tag}",
+                        f"-DTG_TABLE_GROUP=group_{tag}"]
                 units.append((f"inst_tile_{tag}", os.path.join(CSRC, "inst_tile.hip"), defs))
     return units
 

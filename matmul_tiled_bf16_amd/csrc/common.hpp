@@ -32,6 +32,28 @@ struct GemmArgs {
 
 using KernelFn = void (*)(GemmArgs);
 
+// A grouped launch: up to kGroupMax independent products of different shapes
+// (same types and transposes) in one grid.  Work items are numbered problem
+// by problem; problem i owns items [first, first + tiles), its tiles in
+// column-major order.  The table travels in the kernel-argument segment, so the launch
+// needs no device memory of its own.
+constexpr int kGroupMax = 32;
+struct GroupProblem {
+  const uint16_t* A;
+  const uint16_t* B;
+  void* C;
+  int64_t lda, ldb, ldc;
+  int32_t M, N, K;
+  int32_t first;  // first work item of this problem
+};
+struct GroupArgs {
+  GemmArgs g;      // shared launch fields (rotate_k and persist are 0)
+  int32_t count;   // problems in the table, 1 .. kGroupMax
+  int32_t total;   // work items of all problems
+  GroupProblem p[kGroupMax];
+};
+using GroupFn = void (*)(GroupArgs);
+
 // ---------------------------------------------------------------- MFMA ---
 // v_mfma_f32_32x32x16: for D = X Y, lane l supplies row (l & 31) of X and
 // column (l & 31) of Y, each as 8 consecutive k starting at 8*(l >> 5);

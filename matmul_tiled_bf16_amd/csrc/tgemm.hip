@@ -22,7 +22,8 @@ namespace tg {
 // objects built from inst_tile.hip and inst_skinny.hip.
 #define TG_DECLARE(in, out, ta, tb)                                                \
   extern const std::array<KernelFn, kNumTiles> tile_##in##_##out##_##ta##tb;       \
-  extern const std::array<KernelFn, kNumGeneric> generic_##in##_##out##_##ta##tb;
+  extern const std::array<KernelFn, kNumGeneric> generic_##in##_##out##_##ta##tb;  \
+  extern const std::array<GroupFn, kNumGroup> group_##in##_##out##_##ta##tb;
 #define TG_DECLARE_IO(in, out) \
   TG_DECLARE(in, out, 0, 0) TG_DECLARE(in, out, 0, 1) TG_DECLARE(in, out, 1, 0) TG_DECLARE(in, out, 1, 1)
 TG_DECLARE_IO(bf16, f32)
@@ -36,7 +37,9 @@ namespace {
 
 using tg::KernelFn;
 using tg::kGenericTiles;
+using tg::kGroupTiles;
 using tg::kNumGeneric;
+using tg::kNumGroup;
 using tg::kNumSkinny;
 using tg::kNumTiles;
 using tg::kSkinny;
@@ -55,6 +58,11 @@ const KernelFn* const kTileTables[2][2][4] = {{TG_ROW(bf16, f32), TG_ROW(bf16, b
                                               {TG_ROW(f16, f32), TG_ROW(f16, f16)}};
 const KernelFn* const kGenericTables[2][2][4] = {{TG_GROW(bf16, f32), TG_GROW(bf16, bf16)},
                                                  {TG_GROW(f16, f32), TG_GROW(f16, f16)}};
+#define TG_GRPROW(in, out)                                                                                \
+  {tg::group_##in##_##out##_00.data(), tg::group_##in##_##out##_01.data(), tg::group_##in##_##out##_10.data(), \
+   tg::group_##in##_##out##_11.data()}
+const tg::GroupFn* const kGroupTables[2][2][4] = {{TG_GRPROW(bf16, f32), TG_GRPROW(bf16, bf16)},
+                                                  {TG_GRPROW(f16, f32), TG_GRPROW(f16, f16)}};
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -363,6 +371,111 @@ static tg_status launch(const gemm_plan_t* plan, int64_t batch, int64_t sA, int6
   }
   hipLaunchKernelGGL(fn, grid, dim3(l.threads), (size_t)l.dyn_lds, stream, a);
   return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
+}
+
+int32_t tg_group_tiles(void) { return kNumGroup; }
+
+// Grouped launch.  Each problem is validated by gemm_plan; every check runs
+// before anything is enqueued.  Problems the vector loader cannot serve run
+// one by one through gemm_run (element-wise loader); the others go out in
+// launches of up to TG_GROUP_MAX problems, in the order given.
+tg_status gemm_group_run(tg_dtype in_type, tg_dtype out_type, int trans_a, int trans_b,
+                         const gemm_group_problem_t* problems, int64_t count, int32_t tile, hipStream_t stream) {
+  if (count < 0 || (count > 0 && !problems)) return TG_ERR_INVALID;
+  if (tile < -1 || tile >= kNumGroup) return TG_ERR_UNSUPPORTED;
+  for (int64_t i = 0; i < count; ++i) {
+    const gemm_group_problem_t& q = problems[i];
+    gemm_plan_t p;
+    const tg_status st = gemm_plan(&p, in_type, out_type, trans_a, trans_b, q.m, q.n, q.k, q.lda, q.ldb, q.ldc);
+    if (st != TG_OK) return st;
+    if (q.m > 0 && q.n > 0 && (!q.C || (q.k > 0 && (!q.A || !q.B)))) return TG_ERR_INVALID;
+    if (cdiv(q.m, 64) * cdiv(q.n, 64) >= ((int64_t)1 << 30)) return TG_ERR_INVALID;  // item count must fit int32
+  }
+  const int io = in_type == TG_BF16 ? 0 : 1, oo = out_type == TG_FP32 ? 0 : 1, tr = 2 * trans_a + trans_b;
+  const int out_size = out_type == TG_FP32 ? 4 : 2;
+
+  tg::GroupArgs g;
+  g.g = tg::GemmArgs{};
+  g.count = 0;
+  int64_t chunk_first[tg::kGroupMax];  // index into `problems` of each table entry
+  auto flush = [&]() -> tg_status {
+    if (g.count == 0) return TG_OK;
+    // tile: by the group's totals, as choose_tile does for one problem
+    int gt = tile;
+    if (gt < 0) {
+      double flops = 0, bytes = 0;
+      int64_t max_m = 0;
+      auto items = [&](int t) {
+        int64_t n = 0;
+        for (int i = 0; i < g.count; ++i) {
+          const gemm_group_problem_t& q = problems[chunk_first[i]];
+          n += cdiv(q.m, kTiles[t].bm) * cdiv(q.n, kTiles[t].bn);
+        }
+        return n;
+      };
+      for (int i = 0; i < g.count; ++i) {
+        const gemm_group_problem_t& q = problems[chunk_first[i]];
+        flops += 2.0 * (double)q.m * (double)q.n * (double)q.k;
+        bytes += 2.0 * ((double)q.m * q.k + (double)q.k * q.n) + (double)out_size * q.m * q.n;
+        max_m = q.m > max_m ? q.m : max_m;
+      }
+      const bool mfma_bound = bytes > 0 && flops / bytes > 312.5;
+      gt = 0;  // 64x64
+      if (max_m > 32) {
+        if (mfma_bound && items(8) >= 512) gt = 3;       // 256x256, 8 waves
+        else if (items(13) >= 256) gt = mfma_bound ? 2 : 1;  // 128x128
+      }
+    }
+    const TileShape& t = kTiles[kGroupTiles[gt]];
+    int64_t total = 0;
+    for (int i = 0; i < g.count; ++i) {
+      const gemm_group_problem_t& q = problems[chunk_first[i]];
+      g.p[i].first = (int32_t)total;
+      total += cdiv(q.m, t.bm) * cdiv(q.n, t.bn);
+      if (total >= ((int64_t)1 << 31)) return TG_ERR_INVALID;
+    }
+    g.total = (int32_t)total;
+    const tg::GroupFn fn = kGroupTables[io][oo][tr][gt];
+    const int lds = tg::lds_bytes_of(t);
+    if (lds > 64 * 1024) {
+      if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+        return TG_ERR_HIP;
+    }
+    const int64_t cap = (int64_t)1 << 30;
+    hipLaunchKernelGGL(fn, dim3((unsigned)(total < cap ? total : cap)), dim3(64 * t.wm * t.wn), (size_t)lds, stream,
+                       g);
+    g.count = 0;
+    return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
+  };
+
+  for (int64_t i = 0; i < count; ++i) {
+    const gemm_group_problem_t& q = problems[i];
+    if (q.m == 0 || q.n == 0) continue;
+    gemm_plan_t p;
+    (void)gemm_plan(&p, in_type, out_type, trans_a, trans_b, q.m, q.n, q.k, q.lda, q.ldb, q.ldc);
+    const bool aligned = (uintptr_t)q.C % 16 == 0 && (q.k == 0 || ((uintptr_t)q.A % 16 == 0 && (uintptr_t)q.B % 16 == 0));
+    if (!(p.flags & TG_FLAG_VEC16) || !aligned || q.m > INT32_MAX || q.n > INT32_MAX || q.k > INT32_MAX) {
+      const tg_status st = gemm_run(&p, q.A, q.B, q.C, stream);
+      if (st != TG_OK) return st;
+      continue;
+    }
+    tg::GroupProblem& e = g.p[g.count];
+    e.A = static_cast<const uint16_t*>(q.A);
+    e.B = static_cast<const uint16_t*>(q.B);
+    e.C = q.C;
+    e.lda = q.lda;
+    e.ldb = q.ldb;
+    e.ldc = q.ldc;
+    e.M = (int32_t)q.m;
+    e.N = (int32_t)q.n;
+    e.K = (int32_t)q.k;
+    chunk_first[g.count] = i;
+    if (++g.count == tg::kGroupMax) {
+      const tg_status st = flush();
+      if (st != TG_OK) return st;
+    }
+  }
+  return flush();
 }
 
 tg_status gemm_run(const gemm_plan_t* plan, const void* A, const void* B, void* C, hipStream_t stream) {

@@ -348,8 +348,16 @@ struct Frags {
   u32x4 a[FM], b[FN];
 };
 
-template <typename In, typename Out, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int DW, bool TA, bool TB>
-__global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_kernel(GemmArgs args) {
+// The kernel body.  KA is GemmArgs (one problem, or a batch of equal
+// shapes) or, with GROUP, GroupArgs (a table of problems, each item looks its
+// problem up; persistent modes and K rotation are off).
+template <typename In, typename Out, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int DW, bool TA,
+          bool TB, bool GROUP, typename KA>
+__device__ __forceinline__ void tile_gemm_body(const KA& kargs) {
+  const GemmArgs& args = [&]() -> const GemmArgs& {
+    if constexpr (GROUP) return kargs.g;
+    else return kargs;
+  }();
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -393,7 +401,11 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
   const int li = lane & 31, lg = lane >> 5;
   const int trh = lane >> 4, trs = lane & 15;
 
-  const int64_t M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
+  // the current item's problem (fixed for a plain launch)
+  int64_t M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb, ldc = args.ldc;
+  const uint16_t* Ap = args.A;
+  const uint16_t* Bp = args.B;
+  void* Cp = args.C;
 
   const int dwave = wave - (NW - DW);  // index among the copy waves (< 0: computes only)
   const bool copier = dwave >= 0;
@@ -428,10 +440,10 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
   // the second transposing read of a fragment is 4 rows further down
   constexpr uint32_t A_TR4 = 4 * OA::CH * 16, B_TR4 = 4 * OB::CH * 16;
 
-  const int64_t nk = (K + BK - 1) / BK, nfull = K / BK;
+  int64_t nk = (K + BK - 1) / BK, nfull = K / BK;
   // bytes the loads of one operand advance per K step
-  const int64_t a_step = A_KC ? (int64_t)BK * 2 : (int64_t)BK * lda * 2;
-  const int64_t b_step = B_KC ? (int64_t)BK * 2 : (int64_t)BK * ldb * 2;
+  int64_t a_step = A_KC ? (int64_t)BK * 2 : (int64_t)BK * lda * 2;
+  int64_t b_step = B_KC ? (int64_t)BK * 2 : (int64_t)BK * ldb * 2;
 
   // Walk order over the K steps.  Normally 0, 1, ...; with rotate_k the
   // full steps are walked from a per-work-group starting step (the partial
@@ -440,7 +452,9 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
   // offsets -- and HBM channels -- at the same time.  Tiles that share
   // panels (grouped launch order) keep the plain order so that neighbours
   // still meet in L2.
-  const int64_t total = (int64_t)args.tiles_m * args.tiles_n * args.batch;
+  int64_t total;
+  if constexpr (GROUP) total = kargs.total;
+  else total = (int64_t)args.tiles_m * args.tiles_n * args.batch;
   // Persistent mode (args.persist): a work-group walks several items and,
   // once an item's K loop is done, issues the next item's prologue copies
   // before this item's stores, so the next K loop starts while the stores
@@ -457,8 +471,8 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
   constexpr int NS = NW - DW;  // waves that never copy
   constexpr bool SPLIT_OK =
       NS > 0 && EPI_PASSES == 1 && ((BM * StagedC<Out, BN>::UPR) % (NS * 64) == 0);
-  const bool persist = PERSIST_OK && args.persist == 1;
-  const bool split = SPLIT_OK && args.persist == 2;
+  const bool persist = !GROUP && PERSIST_OK && args.persist == 1;
+  const bool split = !GROUP && SPLIT_OK && args.persist == 2;
   // the item being computed: matrix, tile origin, walk rotation, and the
   // source pointers / remaining bytes / K - k0 of the next step to load
   int64_t b = 0, m0 = 0, n0 = 0, rot = 0;
@@ -483,12 +497,44 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
   };
   auto setup = [&](int64_t w) {
     int32_t pm, pn;
-    work_coords<8>(w, total, args.tiles_m, args.tiles_n, b, pm, pn);
+    if constexpr (GROUP) {
+      // XCD x (work-groups w = x mod 8) takes a contiguous run of items, so
+      // the tiles of one problem, which share its operands, meet in one L2
+      const int64_t per = total >> 3, rem = total & 7, x = w & 7, local = w >> 3;
+      const int64_t id = x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
+      // the item's problem: the last one whose first item is <= id
+      int32_t q = 0;
+      for (int32_t i = 1; i < kargs.count; ++i)
+        if (kargs.p[i].first <= id) q = i;
+      const GroupProblem& pr = kargs.p[q];
+      M = pr.M;
+      N = pr.N;
+      K = pr.K;
+      lda = pr.lda;
+      ldb = pr.ldb;
+      ldc = pr.ldc;
+      Ap = pr.A;
+      Bp = pr.B;
+      Cp = pr.C;
+      nk = (K + BK - 1) / BK;
+      nfull = K / BK;
+      a_step = A_KC ? (int64_t)BK * 2 : (int64_t)BK * lda * 2;
+      b_step = B_KC ? (int64_t)BK * 2 : (int64_t)BK * ldb * 2;
+      oa.init(copier ? dwave : 0, lane, lda);
+      ob.init(copier ? dwave : 0, lane, ldb);
+      // column-major tiles: the row tiles of one B panel are neighbours
+      const int32_t t = (int32_t)(id - pr.first), tm = (int32_t)((M + BM - 1) / BM);
+      pn = t / tm;
+      pm = t - pn * tm;
+      b = 0;
+    } else {
+      work_coords<8>(w, total, args.tiles_m, args.tiles_n, b, pm, pn);
+    }
     m0 = (int64_t)pm * BM;
     n0 = (int64_t)pn * BN;
-    rot = (args.rotate_k && nfull > 1) ? w % nfull : 0;
-    a_base = (const char*)(args.A + b * args.sA + (A_KC ? m0 * lda : m0));
-    b_base = (const char*)(args.B + b * args.sB + (B_KC ? n0 * ldb : n0));
+    rot = (!GROUP && args.rotate_k && nfull > 1) ? w % nfull : 0;
+    a_base = (const char*)(Ap + b * args.sA + (A_KC ? m0 * lda : m0));
+    b_base = (const char*)(Bp + b * args.sB + (B_KC ? n0 * ldb : n0));
     a_left0 = A_KC ? ((M - 1 - m0) * lda + K) * 2 : ((K - 1) * lda + (M - m0)) * 2;
     b_left0 = B_KC ? ((N - 1 - n0) * ldb + K) * 2 : ((K - 1) * ldb + (N - n0)) * 2;
     ld_step = 0;
@@ -691,7 +737,7 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
     if constexpr (SPLIT_OK) {
       if (split) {
         using L = StagedC<Out, BN>;
-        char* Cb = (char*)args.C + cb * args.sC * (int64_t)sizeof(Out);
+        char* Cb = (char*)Cp + cb * args.sC * (int64_t)sizeof(Out);
         // every wave's reads of the ring are done; stage the tile in it
         __builtin_amdgcn_s_waitcnt(0xC07F);
         block_barrier();
@@ -700,8 +746,8 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
         block_barrier();
         if (!copier) {
           const __amdgpu_buffer_rsrc_t rs =
-              store_rsrc(Cb + (cm0 * args.ldc + cn0) * (int64_t)L::es, ((M - 1 - cm0) * args.ldc + (N - cn0)) * (int64_t)L::es);
-          stage_c_store<Out, BN, BM, NS * 64, 0>(lds, rs, args.ldc, N - cn0, 0, wave * 64 + lane);
+              store_rsrc(Cb + (cm0 * ldc + cn0) * (int64_t)L::es, ((M - 1 - cm0) * ldc + (N - cn0)) * (int64_t)L::es);
+          stage_c_store<Out, BN, BM, NS * 64, 0>(lds, rs, ldc, N - cn0, 0, wave * 64 + lane);
         }
         // the staged tile has been read (the stores themselves may still be
         // in flight) before the copy waves refill the ring
@@ -737,13 +783,13 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
     }
     {
       const int64_t r0 = cm0 + wm0, c0 = cn0 + wn0;
-      char* Cb = (char*)args.C + cb * args.sC * (int64_t)sizeof(Out);
+      char* Cb = (char*)Cp + cb * args.sC * (int64_t)sizeof(Out);
       if (persist) {
         // always ST store instructions (waves outside C store nothing: an
         // empty descriptor drops every access)
         const bool in = r0 < M && c0 < N;
-        store_tile_vec<Out, FM, FN>(in ? Cb + (r0 * args.ldc + c0) * (int64_t)sizeof(Out) : Cb,
-                                    in ? ((M - 1 - r0) * args.ldc + (N - c0)) * (int64_t)sizeof(Out) : 0, args.ldc,
+        store_tile_vec<Out, FM, FN>(in ? Cb + (r0 * ldc + c0) * (int64_t)sizeof(Out) : Cb,
+                                    in ? ((M - 1 - r0) * ldc + (N - c0)) * (int64_t)sizeof(Out) : 0, ldc,
                                     in ? N - c0 : 0, lane, acc);
         goto stored;
       }
@@ -753,18 +799,18 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
           __builtin_amdgcn_s_waitcnt(0xC07F);
           block_barrier();
           store_tile_lds<Out, BM, BN, WM, WN, FM, FN, EPI_PASSES, 0>(
-              lds, Cb + (cm0 * args.ldc + cn0) * (int64_t)sizeof(Out),
-              ((M - 1 - cm0) * args.ldc + (N - cn0)) * (int64_t)sizeof(Out), args.ldc, N - cn0, wave, lane, acc);
+              lds, Cb + (cm0 * ldc + cn0) * (int64_t)sizeof(Out),
+              ((M - 1 - cm0) * ldc + (N - cn0)) * (int64_t)sizeof(Out), ldc, N - cn0, wave, lane, acc);
           goto stored;
         }
       }
       if (N % 4 == 0 || cn0 + BN <= N) {
         if (r0 < M && c0 < N)
-          store_tile_vec<Out, FM, FN>(Cb + (r0 * args.ldc + c0) * (int64_t)sizeof(Out),
-                                      ((M - 1 - r0) * args.ldc + (N - c0)) * (int64_t)sizeof(Out), args.ldc, N - c0,
+          store_tile_vec<Out, FM, FN>(Cb + (r0 * ldc + c0) * (int64_t)sizeof(Out),
+                                      ((M - 1 - r0) * ldc + (N - c0)) * (int64_t)sizeof(Out), ldc, N - c0,
                                       lane, acc);
       } else {
-        store_tile<Out, FM, FN>(Cb, args.ldc, M, N, r0, c0, lane, acc);
+        store_tile<Out, FM, FN>(Cb, ldc, M, N, r0, c0, lane, acc);
       }
     stored:;
     }
@@ -774,6 +820,16 @@ __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_ker
       block_barrier();
     }
   }
+}
+
+template <typename In, typename Out, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int DW, bool TA, bool TB>
+__global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_kernel(GemmArgs args) {
+  tile_gemm_body<In, Out, BM, BN, BK, WM, WN, STAGES, OCC, DW, TA, TB, false>(args);
+}
+
+template <typename In, typename Out, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int DW, bool TA, bool TB>
+__global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) group_gemm_kernel(GroupArgs args) {
+  tile_gemm_body<In, Out, BM, BN, BK, WM, WN, STAGES, OCC, DW, TA, TB, true>(args);
 }
 
 }  // namespace tg

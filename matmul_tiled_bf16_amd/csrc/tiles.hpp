@@ -50,6 +50,13 @@ constexpr TileShape kTiles[] = {
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
+// Tiles a grouped launch may take (indices into kTiles): small and ragged
+// groups, two HBM/MFMA-balanced 128x128 shapes, the large 8-wave tile, and
+// three shapes with three or four work-groups per CU for groups that stream
+// their B operands (more copies in flight per CU).
+constexpr int kGroupTiles[] = {0, 13, 1, 8, 17, 16, 19};
+constexpr int kNumGroup = sizeof(kGroupTiles) / sizeof(kGroupTiles[0]);
+
 constexpr TileShape kGenericTiles[] = {
     {64, 64, 64, 2, 2, 2},
     {128, 128, 64, 2, 2, 2},

@@ -227,6 +227,45 @@ WORKLOADS = {
 }
 
 
+@dataclasses.dataclass
+class GroupedProblem:
+    """A ragged list of products sharing N and K, as in a mixture-of-experts
+    layer: tokens X [T, K] sorted by expert, expert e owns rows
+    [offsets[e], offsets[e+1]) and multiplies them by its weights W[e] [K, N]
+    (NN, row-major); outputs go to the matching rows of Y [T, N]."""
+    name: str
+    X: np.ndarray
+    W: np.ndarray
+    counts: np.ndarray
+    n: int
+    k: int
+    out_dtype: str = "bf16"
+
+    @property
+    def offsets(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.counts)]).astype(np.int64)
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * float(self.counts.sum()) * self.n * self.k
+
+    def algorithmic_bytes(self, out_size: int) -> float:
+        """X and the weights read once, Y written once."""
+        t = float(self.counts.sum())
+        return 2.0 * t * self.k + 2.0 * len(self.counts) * self.k * self.n + out_size * t * self.n
+
+
+def grouped_moe(seed: int = 6, experts: int = 32, tokens: int = 8192, k: int = 1024, n: int = 1024,
+                out_dtype: str = "bf16") -> GroupedProblem:
+    """Ragged expert GEMMs: expert loads from a multinomial over Dirichlet(1)
+    weights (uneven, some experts may get no tokens), X ~ N(0, 1), W ~ N(0, 1/K)."""
+    rng = np.random.default_rng(seed)
+    counts = rng.multinomial(tokens, rng.dirichlet(np.ones(experts))).astype(np.int64)
+    X = draw(rng, (tokens, k), "normal", 1.0)
+    W = draw(rng, (experts, k, n), "normal", 1.0 / float(np.sqrt(k)))
+    return GroupedProblem(f"grouped_moe_e{experts}_t{tokens}_k{k}_n{n}", X, W, counts, n, k, out_dtype)
+
+
 def sample_indices(seed: int, batch: int, m: int, n: int, count: int = 4096,
                    edges: Tuple[int, ...] = (0, 63, 64, 127, 128, 255, 256)) -> np.ndarray:
     """Seeded (b, i, j) triples: ``count`` uniform draws plus tile-edge points.

@@ -27,7 +27,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"gemm_plan", "bmm_plan", "gemm_plan_tile", "gemm_run", "bmm_run", "tg_status_str", "tg_abi_version",
-            "tg_variant_tiles", "attention_fwd"} <= set(names)
+            "tg_variant_tiles", "attention_fwd", "gemm_group_run", "tg_group_tiles"} <= set(names)
     L = tg.lib()
     for n in names:
         assert hasattr(L, n), f"libtgemm.so does not export {n}"
@@ -220,6 +220,46 @@ def test_run_time_checks_that_need_no_gpu():
     assert L.gemm_run(ctypes.byref(e), None, None, None, None) == tg.TG_OK
     st, e = raw_plan(m=64, n=64, k=64)
     assert L.bmm_run(ctypes.byref(e), 0, 0, 0, 0, None, None, None, None) == tg.TG_OK
+
+
+def group_call(problems, tile=-1, count=None, **kw):
+    a = dict(in_type=tg.TG_BF16, out_type=tg.TG_FP32, ta=0, tb=0)
+    a.update(kw)
+    arr = (tg.GroupProblem * max(len(problems), 1))(*[tg.GroupProblem(*q) for q in problems])
+    return tg.lib().gemm_group_run(a["in_type"], a["out_type"], a["ta"], a["tb"], arr if problems else None,
+                                   len(problems) if count is None else count, tile, None)
+
+
+GOOD = (64, 64, 64, 64, 64, 64, 4096, 4096, 4096)
+
+
+def test_group_tile_count():
+    assert tg.group_tiles() == 7
+
+
+@pytest.mark.parametrize("problems,kw,status", [
+    ([], dict(), tg.TG_OK),                                            # nothing to do
+    ([(0, 64, 64, 64, 64, 64, None, None, None)], dict(), tg.TG_OK),  # empty problems launch nothing
+    ([(64, 0, 64, 64, 64, 64, None, None, None)], dict(), tg.TG_OK),
+    ([GOOD], dict(count=-1), tg.TG_ERR_INVALID),
+    ([GOOD, (64, 64, 64, 32, 64, 64, 4096, 4096, 4096)], dict(), tg.TG_ERR_INVALID),  # lda < k
+    ([GOOD, (64, 64, 64, 64, 64, 64, 4096, 4096, None)], dict(), tg.TG_ERR_INVALID),  # null C
+    ([GOOD, (64, 64, 64, 64, 64, 64, None, 4096, 4096)], dict(), tg.TG_ERR_INVALID),  # null A, k > 0
+    ([(-1, 64, 64, 64, 64, 64, 4096, 4096, 4096)], dict(), tg.TG_ERR_INVALID),
+    ([GOOD], dict(tb=2), tg.TG_ERR_INVALID),
+    ([GOOD], dict(tile=7), tg.TG_ERR_UNSUPPORTED),
+    ([GOOD], dict(tile=-2), tg.TG_ERR_UNSUPPORTED),
+    ([GOOD], dict(in_type=tg.TG_FP16, out_type=tg.TG_BF16), tg.TG_ERR_UNSUPPORTED),
+])
+def test_group_argument_checks(problems, kw, status):
+    """Every problem is validated before anything is enqueued (no device call here)."""
+    count = kw.pop("count", None)
+    tile = kw.pop("tile", -1)
+    assert group_call(problems, tile=tile, count=count, **kw) == status
+
+
+def test_group_null_array_with_count():
+    assert tg.lib().gemm_group_run(tg.TG_BF16, tg.TG_FP32, 0, 0, None, 3, -1, None) == tg.TG_ERR_INVALID
 
 
 def attn_call(**kw):
