@@ -131,6 +131,22 @@ def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, *, n_q: int, n_k: int
     return out.reshape(batch, n_q, head_dim) if full else out
 
 
+def epilogue(P: np.ndarray, alpha: float = 1.0, beta: float = 0.0, C_in: Optional[np.ndarray] = None,
+             bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """alpha * P + beta * C_in + bias[j], elementwise in fp64 (the scaled-and-shifted
+    product the pages call a trivial epilogue: "Finetuning Your Program", the
+    alpha/beta note).  P: the exact product from gemm() (any leading shape,
+    columns last); C_in: prior contents of C as values (read only when
+    beta != 0, as BLAS defines it: with beta = 0, NaN or Inf in C never
+    reach the result); bias: one value per column, added to every row."""
+    out = float(alpha) * np.asarray(P, dtype=np.float64)
+    if beta != 0.0:
+        out = out + float(beta) * np.asarray(C_in, dtype=np.float64)
+    if bias is not None:
+        out = out + np.asarray(bias, dtype=np.float64).reshape((1,) * (out.ndim - 1) + (-1,))
+    return out
+
+
 def gemm_problem(p, idx: Optional[np.ndarray] = None) -> np.ndarray:
     """Reference for a ``synth.Problem``."""
     return gemm(p.A, p.B, m=p.m, n=p.n, k=p.k, trans_a=p.trans_a, trans_b=p.trans_b, lda=p.lda,

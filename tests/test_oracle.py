@@ -388,3 +388,36 @@ def test_attention_rows_and_strides_address_the_right_data():
     assert np.array_equal(got, full)
     with pytest.raises(IndexError):
         oracle.attention(Q, K, V, n_q=n_q, n_k=n_k, head_dim=d, scale=0.3, batch=b, rows=np.array([[3, 0]]))
+
+
+# ------------------------------------------------------------- epilogue ---
+
+def test_epilogue_identity_is_the_product():
+    rng = np.random.default_rng(40)
+    A = synth.draw(rng, (5, 7), "normal", 1.0)
+    B = synth.draw(rng, (7, 3), "normal", 1.0)
+    P = oracle.gemm(A, B, m=5, n=3, k=7)[0]
+    assert np.array_equal(oracle.epilogue(P), P)
+    assert np.array_equal(oracle.epilogue(P, 1.0, 0.0, np.full(P.shape, np.nan)), P)  # C not read at beta = 0
+
+
+def test_epilogue_worked_example_by_hand():
+    """A = I (2x2), B = [[1, 2], [3, 4]], C = [[10, 20], [30, 40]], bias = [0.5, -1]:
+    2 * B - 1 * C + bias = [[-7.5, -17], [-23.5, -33]]."""
+    A = oracle.round_to(np.eye(2), "bf16")
+    B = oracle.round_to(np.array([[1.0, 2.0], [3.0, 4.0]]), "bf16")
+    P = oracle.gemm(A, B, m=2, n=2, k=2)[0]
+    out = oracle.epilogue(P, 2.0, -1.0, np.array([[10.0, 20.0], [30.0, 40.0]]), np.array([0.5, -1.0]))
+    assert np.array_equal(out, np.array([[-7.5, -17.0], [-23.5, -33.0]]))
+
+
+def test_epilogue_k0_and_batches():
+    """K = 0: the product is zero, so the result is beta * C + bias in every
+    batch (bias broadcast over rows and batches)."""
+    A = np.zeros((3, 4, 0), dtype=np.uint16)
+    B = np.zeros((3, 0, 5), dtype=np.uint16)
+    P = oracle.gemm(A, B, m=4, n=5, k=0, batch=3, lda=1, ldb=5, stride_a=0, stride_b=0)
+    C = np.arange(60, dtype=np.float64).reshape(3, 4, 5)
+    bias = np.array([1.0, 2.0, 3.0, 4.0, 5.0])
+    out = oracle.epilogue(P, 3.0, 0.5, C, bias)
+    assert np.array_equal(out, 0.5 * C + bias[None, None, :])
