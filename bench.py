@@ -75,6 +75,9 @@ def main():
     ap.add_argument("--no-prefetch", action="store_true", help="clear the plan's prefetch flag")
     ap.add_argument("--prefetch", action="store_true", help="set the plan's persistent and prefetch flags")
     ap.add_argument("--group-tile", type=int, default=-1, help="force the grouped launch's tile (group_moe)")
+    ap.add_argument("--alpha", type=float, default=1.0, help="epilogue: C = alpha*AB + beta*C + bias")
+    ap.add_argument("--beta", type=float, default=0.0, help="epilogue: scale of C's prior contents")
+    ap.add_argument("--bias", action="store_true", help="epilogue: add a per-column bias")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to calibrate FETCH_SIZE/WRITE_SIZE)")
@@ -116,6 +119,11 @@ def main():
 
     flops = roofline.gemm_flops(p.m, p.n, p.k, p.batch)
     nbytes = roofline.gemm_bytes(p.m, p.n, p.k, 2, out_size, p.batch)
+    epi = args.alpha != 1.0 or args.beta != 0.0 or args.bias
+    if args.beta != 0.0:
+        nbytes += out_size * p.m * p.n * p.batch  # C is read as well as written
+    if args.bias:
+        nbytes += out_size * p.n
     bound = roofline.bound(p.m, p.n, p.k, 2, out_size, p.batch, PEAK_MFMA, PEAK_HBM)
     rotate = args.rotate or (4 if bound == "hbm" else 1)
 
@@ -124,6 +132,10 @@ def main():
     Cs = [torch.empty((p.batch, p.m, p.n) if p.batch > 1 else (p.m, p.n), dtype=tout, device=dev)
           for _ in range(min(rotate, 2))]
     stream = torch.cuda.current_stream()
+    bias = torch.randn(p.n, device=dev).to(tout) if args.bias else None
+    if args.beta != 0.0:
+        for C in Cs:
+            C.copy_(torch.randn(C.shape, device=dev).to(tout))
 
     def step(i):
         pl = tg.plan(p.m, p.n, p.k, trans_a=p.trans_a, trans_b=p.trans_b, in_dtype=tin, out_dtype=tout,
@@ -138,7 +150,13 @@ def main():
             pl.flags |= tg.FLAG_PERSIST | tg.FLAG_PREFETCH
         B = Bs[i % len(Bs)]
         C = Cs[i % len(Cs)]
-        if p.batch == 1:
+        if epi:
+            if p.batch == 1:
+                tg.gemm_run_ex(pl, A, B, C, alpha=args.alpha, beta=args.beta, bias=bias, stream=stream)
+            else:
+                tg.bmm_run_ex(pl, p.batch, p.stride_a, p.stride_b, p.stride_c, A, B, C, alpha=args.alpha,
+                              beta=args.beta, bias=bias, stream=stream)
+        elif p.batch == 1:
             tg.gemm_run(pl, A, B, C, stream)
         else:
             tg.bmm_run(pl, p.batch, p.stride_a, p.stride_b, p.stride_c, A, B, C, stream)
@@ -189,7 +207,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": p.name, "m": p.m, "n": p.n, "k": p.k, "batch": p.batch, "op": trans,
                    "in_dtype": p.in_dtype, "out_dtype": p.out_dtype, "b_copies": len(Bs),
-                   "variant": int(pl.variant), "tile_index": int(pl.tile), "plan_flags": int(pl.flags)},
+                   "variant": int(pl.variant), "tile_index": int(pl.tile), "plan_flags": int(pl.flags),
+                   **({"epilogue": {"alpha": args.alpha, "beta": args.beta, "bias": bool(args.bias)}} if epi else {})},
         "tflops": round(tflops, 2),
         "pct_mfma_peak": round(100 * flops / (ms_per_step / 1e3) / PEAK_MFMA, 2),
         "gbps": round(gbps, 1),

@@ -12,7 +12,8 @@
  * each operand by its own batch stride (same page, section 3).  Inputs are
  * bf16 or fp16, products are accumulated in fp32, and the fp32 sum is written
  * as fp32 or rounded to the input type (round to nearest, ties to even).  C is
- * overwritten; there is no alpha/beta.
+ * overwritten, or, through gemm_run_ex/bmm_run_ex, combined with its prior
+ * contents by an alpha/beta/bias epilogue.
  *
  * Storage and leading dimensions (all in elements, all row-major):
  *   trans_a = 0: A is M x K, element (i,k) at A[i*lda + k],  lda >= max(1, K)
@@ -222,6 +223,35 @@ tg_status attention_fwd(tg_dtype in_type, tg_dtype out_type, int64_t batch, int6
                         int64_t head_dim, float scale, const void* Q, int64_t ldq, int64_t stride_q,
                         const void* K, int64_t ldk, int64_t stride_k, const void* V, int64_t ldv,
                         int64_t stride_v, void* O, int64_t ldo, int64_t stride_o, hipStream_t stream);
+
+/*
+ * Optional epilogue of gemm_run_ex / bmm_run_ex, applied to the fp32 sum
+ * before the output rounding:
+ *     C = alpha * op(A) op(B) + beta * C + bias[j]
+ * (the scaled-and-shifted product the pages count as a trivial epilogue:
+ * "Finetuning Your Program", the alpha/beta note).  C's prior contents are
+ * read only when beta != 0 (with beta = 0, NaN or Inf in C are ignored, as
+ * in BLAS).  bias: null, or a device array of n values of the output type
+ * (fp32 for an fp32 output, else the input type), naturally aligned, added to
+ * every row (and, in a batch, to every matrix).  alpha = 1, beta = 0 and no
+ * bias is exactly the plain product.
+ */
+typedef struct {
+  float alpha;
+  float beta;
+  const void* bias;
+} gemm_epilogue_t;
+
+/*
+ * gemm_run_ex / bmm_run_ex -- gemm_run / bmm_run with an epilogue (null: none).
+ * Same errors, plus TG_ERR_INVALID for a misaligned bias.  With an epilogue
+ * the persistent launch modes (TG_FLAG_PERSIST, TG_FLAG_PREFETCH) are not
+ * used; the result does not depend on them.
+ */
+tg_status gemm_run_ex(const gemm_plan_t* plan, const gemm_epilogue_t* epi, const void* A, const void* B, void* C,
+                      hipStream_t stream);
+tg_status bmm_run_ex(const gemm_plan_t* plan, const gemm_epilogue_t* epi, int64_t batch, int64_t stride_a,
+                     int64_t stride_b, int64_t stride_c, const void* A, const void* B, void* C, hipStream_t stream);
 
 /* Static text for a status code ("ok", "invalid argument", ...). */
 const char* tg_status_str(tg_status s);

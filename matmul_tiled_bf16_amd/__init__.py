@@ -60,6 +60,11 @@ class GroupProblem(ctypes.Structure):
                 ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p)]
 
 
+class Epilogue(ctypes.Structure):
+    """Mirror of gemm_epilogue_t: C = alpha * op(A) op(B) + beta * C + bias[j]."""
+    _fields_ = [("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("bias", ctypes.c_void_p)]
+
+
 class TgError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__(f"{what}: {status_str(status)} (status {status})")
@@ -95,6 +100,10 @@ def lib() -> ctypes.CDLL:
                                i64, i64, i64, i64, i64, i64, i64]
         L.gemm_plan_tile.restype = ctypes.c_int
         L.gemm_plan_tile.argtypes = [ctypes.POINTER(GemmPlan), i32, i32]
+        L.gemm_run_ex.restype = ctypes.c_int
+        L.gemm_run_ex.argtypes = [ctypes.POINTER(GemmPlan), ctypes.POINTER(Epilogue), p, p, p, p]
+        L.bmm_run_ex.restype = ctypes.c_int
+        L.bmm_run_ex.argtypes = [ctypes.POINTER(GemmPlan), ctypes.POINTER(Epilogue), i64, i64, i64, i64, p, p, p, p]
         L.gemm_group_run.restype = ctypes.c_int
         L.gemm_group_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.POINTER(GroupProblem), i64, i32, p]
@@ -182,6 +191,30 @@ def bmm_run(p: GemmPlan, batch: int, stride_a: int, stride_b: int, stride_c: int
         raise TgError(st, "bmm_run")
 
 
+def _epilogue(alpha, beta, bias):
+    if alpha == 1.0 and beta == 0.0 and bias is None:
+        return None
+    return Epilogue(alpha, beta, _ptr(bias) if bias is not None else None)
+
+
+def gemm_run_ex(p: GemmPlan, A, B, C, *, alpha: float = 1.0, beta: float = 0.0, bias=None, stream=None) -> None:
+    """gemm_run_ex(): C = alpha * op(A) op(B) + beta * C + bias (bias: n values of C's dtype)."""
+    e = _epilogue(alpha, beta, bias)
+    st = lib().gemm_run_ex(ctypes.byref(p), ctypes.byref(e) if e else None, _ptr(A), _ptr(B), _ptr(C),
+                           _stream_handle(stream))
+    if st != TG_OK:
+        raise TgError(st, "gemm_run_ex")
+
+
+def bmm_run_ex(p: GemmPlan, batch: int, stride_a: int, stride_b: int, stride_c: int, A, B, C, *,
+               alpha: float = 1.0, beta: float = 0.0, bias=None, stream=None) -> None:
+    e = _epilogue(alpha, beta, bias)
+    st = lib().bmm_run_ex(ctypes.byref(p), ctypes.byref(e) if e else None, batch, stride_a, stride_b, stride_c,
+                          _ptr(A), _ptr(B), _ptr(C), _stream_handle(stream))
+    if st != TG_OK:
+        raise TgError(st, "bmm_run_ex")
+
+
 def _check_matrix(X, name):
     if not X.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
@@ -193,8 +226,10 @@ def _ld(X) -> int:
     return max(X.stride(-2), X.shape[-1], 1)
 
 
-def gemm(A, B, *, trans_a: bool = False, trans_b: bool = False, out_dtype=None, out=None, stream=None):
-    """C = op(A) @ op(B) for 2-D row-major tensors; returns C (new, or ``out``)."""
+def gemm(A, B, *, trans_a: bool = False, trans_b: bool = False, out_dtype=None, out=None, alpha: float = 1.0,
+         beta: float = 0.0, bias=None, stream=None):
+    """C = alpha * op(A) @ op(B) + beta * C + bias for 2-D row-major tensors; returns C
+    (new, or ``out``, whose prior contents are read when beta != 0)."""
     import torch
     _check_matrix(A, "A")
     _check_matrix(B, "B")
@@ -205,13 +240,17 @@ def gemm(A, B, *, trans_a: bool = False, trans_b: bool = False, out_dtype=None, 
     if kb != k:
         raise ValueError(f"inner dimensions differ: {k} vs {kb}")
     out_dtype = out_dtype or torch.float32
+    if beta != 0.0 and out is None:
+        raise ValueError("beta != 0 needs `out` (the C to scale)")
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=A.device)
     elif out.shape != (m, n) or out.dtype != out_dtype:
         raise ValueError("out has the wrong shape or dtype")
+    if bias is not None and (bias.dtype != out_dtype or bias.numel() != n or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous tensor of n values of the output dtype")
     p = plan(m, n, k, trans_a=trans_a, trans_b=trans_b, in_dtype=A.dtype, out_dtype=out_dtype, lda=_ld(A),
              ldb=_ld(B), ldc=_ld(out))
-    gemm_run(p, A, B, out, stream)
+    gemm_run_ex(p, A, B, out, alpha=alpha, beta=beta, bias=bias, stream=stream)
     return out
 
 

@@ -28,6 +28,11 @@ struct GemmArgs {
   int32_t tiles_m, tiles_n;
   int32_t rotate_k;  // nonzero: each work-group starts its walk over K at a different step
   int32_t persist;   // nonzero: the next item's first stages are issued before this item's stores
+  // epilogue: C = alpha * acc + beta * C + bias[col] when epi != 0 (C is
+  // read only if beta != 0; bias, of the output type, may be null)
+  int32_t epi;
+  float alpha, beta;
+  const void* bias;
 };
 
 using KernelFn = void (*)(GemmArgs);
@@ -104,6 +109,39 @@ __device__ __forceinline__ void store_out<__bf16>(void* C, int64_t off, float v)
 template <>
 __device__ __forceinline__ void store_out<_Float16>(void* C, int64_t off, float v) {
   static_cast<_Float16*>(C)[off] = (_Float16)v;
+}
+
+template <typename Out>
+__device__ __forceinline__ float load_out(const void* C, int64_t off) {
+  return (float)static_cast<const Out*>(C)[off];
+}
+
+// The epilogue on a wave's FM x FN accumulator blocks (acc holds C^T, see
+// mfma32), in fp32 before any store path: acc = alpha*acc + beta*C + bias.
+// Rows/columns past M/N are not read; their values are never stored.
+template <typename Out, int FM, int FN>
+__device__ __forceinline__ void epilogue_acc(const GemmArgs& args, const void* Cb, int64_t ldc, int64_t M, int64_t N,
+                                             int64_t r0, int64_t c0, int lane, f32x16 (&acc)[FM][FN]) {
+  const int li = lane & 31, lg = lane >> 5;
+  const float alpha = args.alpha, beta = args.beta;
+  const bool use_c = beta != 0.f, use_bias = args.bias != nullptr;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t row = r0 + i * 32 + li;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t col = c0 + j * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+        float v = alpha * acc[i][j][r];
+        if (row < M && col < N) {
+          if (use_c) v = __builtin_fmaf(beta, load_out<Out>(Cb, row * ldc + col), v);
+          if (use_bias) v += load_out<Out>(args.bias, col);
+        }
+        acc[i][j][r] = v;
+      }
+    }
+  }
 }
 
 // --------------------------------------------------------- LDS helpers ---

@@ -114,6 +114,7 @@ __global__ void __launch_bounds__(WM * WN * 64) generic_gemm_kernel(GemmArgs arg
       __syncthreads();
     }
     void* Cb = (char*)args.C + b * args.sC * (int64_t)sizeof(Out);
+    if (args.epi) epilogue_acc<Out, FM, FN>(args, Cb, args.ldc, M, N, m0 + wm0, n0 + wn0, lane, acc);
     store_tile<Out, FM, FN>(Cb, args.ldc, M, N, m0 + wm0, n0 + wn0, lane, acc);
   }
 }

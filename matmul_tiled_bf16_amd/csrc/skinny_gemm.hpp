@@ -230,7 +230,14 @@ __global__ void __launch_bounds__(WAVES * 64) skinny_gemm_kernel(GemmArgs args) 
 #pragma unroll
       for (int it = rb; it < KB * NB; it += NB) sum += red[((it * MB + i) * 64 + src_lane) * 4 + q];
       const int64_t gc = n0 + col;
-      if (row < M && gc < N) store_out<Out>(Cb, row * args.ldc + gc, sum);
+      if (row < M && gc < N) {
+        if (args.epi) {  // alpha * sum + beta * C + bias, as epilogue_acc
+          sum *= args.alpha;
+          if (args.beta != 0.f) sum = __builtin_fmaf(args.beta, load_out<Out>(Cb, row * args.ldc + gc), sum);
+          if (args.bias) sum += load_out<Out>(args.bias, gc);
+        }
+        store_out<Out>(Cb, row * args.ldc + gc, sum);
+      }
     }
     __syncthreads();
   }

@@ -278,8 +278,8 @@ static int compute_units() {
   return cus;
 }
 
-static tg_status launch(const gemm_plan_t* plan, int64_t batch, int64_t sA, int64_t sB, int64_t sC, const void* A,
-                        const void* B, void* C, hipStream_t stream) {
+static tg_status launch(const gemm_plan_t* plan, const gemm_epilogue_t* epi, int64_t batch, int64_t sA, int64_t sB,
+                        int64_t sC, const void* A, const void* B, void* C, hipStream_t stream) {
   if (!plan || plan->abi_version != TG_ABI_VERSION) return TG_ERR_INVALID;
   if (batch < 0 || sA < 0 || sB < 0 || sC < 0) return TG_ERR_INVALID;
   const gemm_plan_t& p = *plan;
@@ -324,6 +324,12 @@ static tg_status launch(const gemm_plan_t* plan, int64_t batch, int64_t sA, int6
   a.batch = batch;
   a.rotate_k = (variant == TG_VARIANT_TILE && (p.flags & TG_FLAG_ROTATE_K)) ? 1 : 0;
   a.persist = 0;
+  // an identity epilogue (alpha 1, beta 0, no bias) is no epilogue
+  a.epi = epi && !(epi->alpha == 1.f && epi->beta == 0.f && !epi->bias) ? 1 : 0;
+  a.alpha = epi ? epi->alpha : 1.f;
+  a.beta = epi ? epi->beta : 0.f;
+  a.bias = epi ? epi->bias : nullptr;
+  if (a.epi && a.bias && (uintptr_t)a.bias % (p.out_type == TG_FP32 ? 4 : 2) != 0) return TG_ERR_INVALID;
 
   const Launch l = launch_shape(variant, tile);
   const int io = p.in_type == TG_BF16 ? 0 : 1, oo = p.out_type == TG_FP32 ? 0 : 1;
@@ -349,7 +355,7 @@ static tg_status launch(const gemm_plan_t* plan, int64_t batch, int64_t sA, int6
     // keeps every item on the XCD the kernel's tile order assumes)
     const int64_t total = groups * batch;
     int64_t cap = (int64_t)1 << 30;
-    if (variant == TG_VARIANT_TILE && (p.flags & TG_FLAG_PERSIST)) {
+    if (variant == TG_VARIANT_TILE && (p.flags & TG_FLAG_PERSIST) && !a.epi) {
       // persistent: one work-group per resident slot (a multiple of 8)
       const int64_t slots = (int64_t)compute_units() * kTiles[tile].occ;
       if (slots > 0 && total >= 2 * slots) {
@@ -479,12 +485,22 @@ tg_status gemm_group_run(tg_dtype in_type, tg_dtype out_type, int trans_a, int t
 }
 
 tg_status gemm_run(const gemm_plan_t* plan, const void* A, const void* B, void* C, hipStream_t stream) {
-  return launch(plan, 1, 0, 0, 0, A, B, C, stream);
+  return launch(plan, nullptr, 1, 0, 0, 0, A, B, C, stream);
 }
 
 tg_status bmm_run(const gemm_plan_t* plan, int64_t batch, int64_t stride_a, int64_t stride_b, int64_t stride_c,
                   const void* A, const void* B, void* C, hipStream_t stream) {
-  return launch(plan, batch, stride_a, stride_b, stride_c, A, B, C, stream);
+  return launch(plan, nullptr, batch, stride_a, stride_b, stride_c, A, B, C, stream);
+}
+
+tg_status gemm_run_ex(const gemm_plan_t* plan, const gemm_epilogue_t* epi, const void* A, const void* B, void* C,
+                      hipStream_t stream) {
+  return launch(plan, epi, 1, 0, 0, 0, A, B, C, stream);
+}
+
+tg_status bmm_run_ex(const gemm_plan_t* plan, const gemm_epilogue_t* epi, int64_t batch, int64_t stride_a,
+                     int64_t stride_b, int64_t stride_c, const void* A, const void* B, void* C, hipStream_t stream) {
+  return launch(plan, epi, batch, stride_a, stride_b, stride_c, A, B, C, stream);
 }
 
 }  // extern "C"

@@ -227,6 +227,74 @@ __device__ __forceinline__ void store_tile_vec(const void* Ctile, int64_t bytes,
   }
 }
 
+// The epilogue (alpha*acc + beta*C + bias, see epilogue_acc) with vector
+// reads of C shaped like store_tile_vec's writes: per group of 4 registers,
+// one 16-byte (fp32) or 8-byte (16-bit) load of 4 consecutive columns of one
+// row.  Same descriptor and column mask as store_tile_vec (rows past M read
+// zero, groups at or past n_left get an out-of-range offset); the bias is
+// read element by element through a descriptor that ends at column N.
+template <typename Out, int FM, int FN>
+__device__ __forceinline__ void epilogue_acc_vec(const GemmArgs& args, const void* Ctile, int64_t bytes, int64_t ldc,
+                                                 int64_t n_left, int64_t c0, int lane, f32x16 (&acc)[FM][FN]) {
+  const int li = lane & 31, lg = lane >> 5;
+  constexpr uint32_t es = sizeof(Out);
+  const float alpha = args.alpha, beta = args.beta;
+  float bias[FN][16];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bias[j][r] = 0.f;
+  if (args.bias) {
+    const __amdgpu_buffer_rsrc_t rb =
+        store_rsrc((const char*)args.bias + c0 * (int64_t)es, n_left > 0 ? n_left * (int64_t)es : 0);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t off = (uint32_t)(j * 32 + 8 * (r >> 2) + 4 * lg + (r & 3)) * es;
+        if constexpr (es == 4) {
+          bias[j][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (int)off, 0, 0));
+        } else {
+          const uint16_t h = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)off, 0, 0);
+          bias[j][r] = (float)__builtin_bit_cast(Out, h);
+        }
+      }
+  }
+  const __amdgpu_buffer_rsrc_t rs = store_rsrc(Ctile, bytes);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const uint32_t rowoff = (uint32_t)((i * 32 + li) * ldc) * es;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = j * 32 + 8 * g + 4 * lg;
+        float c[4] = {0.f, 0.f, 0.f, 0.f};
+        if (beta != 0.f) {
+          const uint32_t off = col < n_left ? rowoff + (uint32_t)col * es : kOutOfRange;
+          // (whole-vector bit casts: this compiler mislowers a bit cast of
+          // a single vector element)
+          if constexpr (es == 4) {
+            const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) c[q] = v[q];
+          } else {
+            typedef Out out4 __attribute__((ext_vector_type(4)));
+            const out4 v = __builtin_bit_cast(out4, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, 0));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) c[q] = (float)v[q];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = 4 * g + q;
+          acc[i][j][r] = __builtin_fmaf(beta, c[q], alpha * acc[i][j][r]) + bias[j][r];
+        }
+      }
+    }
+  }
+}
+
 // LDS-staged store of the work-group's BM x BN tile ("Triton Optimization
 // Reference", section 5: the epilogue goes out in subtiles through shared
 // memory).  The MFMA result layout gives each lane four consecutive columns
@@ -471,8 +539,8 @@ __device__ __forceinline__ void tile_gemm_body(const KA& kargs) {
   constexpr int NS = NW - DW;  // waves that never copy
   constexpr bool SPLIT_OK =
       NS > 0 && EPI_PASSES == 1 && ((BM * StagedC<Out, BN>::UPR) % (NS * 64) == 0);
-  const bool persist = !GROUP && PERSIST_OK && args.persist == 1;
-  const bool split = !GROUP && SPLIT_OK && args.persist == 2;
+  const bool persist = !GROUP && PERSIST_OK && args.persist == 1 && !args.epi;
+  const bool split = !GROUP && SPLIT_OK && args.persist == 2 && !args.epi;
   // the item being computed: matrix, tile origin, walk rotation, and the
   // source pointers / remaining bytes / K - k0 of the next step to load
   int64_t b = 0, m0 = 0, n0 = 0, rot = 0;
@@ -730,6 +798,18 @@ __device__ __forceinline__ void tile_gemm_body(const KA& kargs) {
       for (; kt < nk; ++kt) stage_dyn(kt);
     }
 
+    if (!GROUP && args.epi) {
+      const char* Cb = (const char*)Cp + b * args.sC * (int64_t)sizeof(Out);
+      const int64_t r0 = m0 + wm0, c0 = n0 + wn0;
+      if (N % 4 == 0 || n0 + BN <= N) {  // 4-column groups never straddle column N
+        if (r0 < M && c0 < N)
+          epilogue_acc_vec<Out, FM, FN>(args, Cb + (r0 * ldc + c0) * (int64_t)sizeof(Out),
+                                        ((M - 1 - r0) * ldc + (N - c0)) * (int64_t)sizeof(Out), ldc, N - c0, c0,
+                                        lane, acc);
+      } else {
+        epilogue_acc<Out, FM, FN>(args, Cb, ldc, M, N, r0, c0, lane, acc);
+      }
+    }
     // this item's origin (in persistent mode the state moves on below)
     const int64_t cb = b, cm0 = m0, cn0 = n0;
     prefetched = false;
