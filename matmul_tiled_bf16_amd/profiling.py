@@ -9,14 +9,14 @@
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/cfetch -o run -- python bench.py --copy-calibration
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/cwrite -o run -- python bench.py --copy-calibration
 
-    python -m matmul_tiled_bf16_amd.profiling stats OUT/trace [gemm|attention] > profiles/<kernel>_<workload>_stats.txt
+    python -m matmul_tiled_bf16_amd.profiling stats OUT/trace [gemm|group|attention] > profiles/<kernel>_<workload>_stats.txt
     python -m matmul_tiled_bf16_amd.profiling traffic OUT <workload> > profiles/<workload>_traffic.txt
 
 FETCH_SIZE / WRITE_SIZE are reported in KiB per dispatch; the copy kernel
 moves a known number of bytes, and the ratio of that number to what the
 counter reads for it scales the kernel's reading to bytes.  A traffic file
-records a hash of the sources its kernel family (GEMM or attention) is built
-from; bench.py reports traffic only while those sources still match.
+records a hash of the sources its kernel family (GEMM, grouped GEMM or
+attention) is built from; bench.py reports traffic only while those sources still match.
 """
 from __future__ import annotations
 
@@ -34,6 +34,7 @@ COPY_BYTES = 1 << 30  # bytes read and written by one calibration copy
 FAMILIES = {
     "gemm": (("tile_gemm_kernel", "skinny_gemm_kernel", "generic_gemm_kernel"),
              lambda f: not os.path.basename(f).startswith("attention")),
+    "group": (("group_gemm_kernel",), lambda f: not os.path.basename(f).startswith("attention")),
     "attention": (("attn_fwd_kernel",),
                   lambda f: os.path.basename(f) in ("attention.hpp", "attention.hip", "tile_gemm.hpp",
                                                     "common.hpp")),
@@ -41,7 +42,11 @@ FAMILIES = {
 
 
 def family_of(workload: str) -> str:
-    return "attention" if workload.startswith("attn_fwd") else "gemm"
+    if workload.startswith("attn_fwd"):
+        return "attention"
+    if workload.startswith("grouped"):
+        return "group"
+    return "gemm"
 
 
 def source_hash(family: str = "gemm") -> str:
