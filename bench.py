@@ -74,6 +74,7 @@ def main():
     ap.add_argument("--no-persist", action="store_true", help="clear the plan's persistent-launch flags")
     ap.add_argument("--no-prefetch", action="store_true", help="clear the plan's prefetch flag")
     ap.add_argument("--prefetch", action="store_true", help="set the plan's persistent and prefetch flags")
+    ap.add_argument("--stream-c", type=int, default=-1, help="force the plan's non-temporal C flag (0/1)")
     ap.add_argument("--group-tile", type=int, default=-1, help="force the grouped launch's tile (group_moe)")
     ap.add_argument("--alpha", type=float, default=1.0, help="epilogue: C = alpha*AB + beta*C + bias")
     ap.add_argument("--beta", type=float, default=0.0, help="epilogue: scale of C's prior contents")
@@ -148,6 +149,10 @@ def main():
             pl.flags &= ~tg.FLAG_PREFETCH
         if args.prefetch:
             pl.flags |= tg.FLAG_PERSIST | tg.FLAG_PREFETCH
+        if args.stream_c == 0:
+            pl.flags &= ~tg.FLAG_STREAM_C
+        elif args.stream_c == 1:
+            pl.flags |= tg.FLAG_STREAM_C
         B = Bs[i % len(Bs)]
         C = Cs[i % len(Cs)]
         if epi:

@@ -68,9 +68,11 @@ typedef enum {
                                 launch one work-group per resident slot and let each loop over
                                 tiles (no dispatch gap between tiles) */
 #define TG_FLAG_PREFETCH 0x10 /* with PERSIST: issue the next tile's first copies before this
-                                 tile's stores (stores go straight from registers).  A caller may
-                                 clear PERSIST, PREFETCH or ROTATE_K in a plan; the result is the
-                                 same up to fp32 summation order. */
+                                 tile's stores (stores go straight from registers). */
+#define TG_FLAG_STREAM_C 0x20 /* tile kernel: store C non-temporally (outputs much larger than the
+                                 L2s: the stream of C then does not evict the operands).  A caller
+                                 may clear or set PERSIST, PREFETCH, ROTATE_K or STREAM_C in a plan;
+                                 the result is the same up to fp32 summation order. */
 
 /*
  * A plan: caller-owned plain data, filled by gemm_plan(), read by gemm_run()

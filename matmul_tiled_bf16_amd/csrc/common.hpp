@@ -33,6 +33,7 @@ struct GemmArgs {
   int32_t epi;
   float alpha, beta;
   const void* bias;
+  int32_t stream_c;  // nonzero: LDS-staged C stores are non-temporal
 };
 
 using KernelFn = void (*)(GemmArgs);

@@ -878,9 +878,16 @@ __device__ __forceinline__ void tile_gemm_body(const KA& kargs) {
           // every wave's reads of the last stage are done before LDS is reused
           __builtin_amdgcn_s_waitcnt(0xC07F);
           block_barrier();
-          store_tile_lds<Out, BM, BN, WM, WN, FM, FN, EPI_PASSES, 0>(
-              lds, Cb + (cm0 * ldc + cn0) * (int64_t)sizeof(Out),
-              ((M - 1 - cm0) * ldc + (N - cn0)) * (int64_t)sizeof(Out), ldc, N - cn0, wave, lane, acc);
+          // non-temporal stores (args.stream_c) for outputs far larger than
+          // the L2s, so that they do not evict the operands' panels
+          if (args.stream_c)
+            store_tile_lds<Out, BM, BN, WM, WN, FM, FN, EPI_PASSES, 2>(
+                lds, Cb + (cm0 * ldc + cn0) * (int64_t)sizeof(Out),
+                ((M - 1 - cm0) * ldc + (N - cn0)) * (int64_t)sizeof(Out), ldc, N - cn0, wave, lane, acc);
+          else
+            store_tile_lds<Out, BM, BN, WM, WN, FM, FN, EPI_PASSES, 0>(
+                lds, Cb + (cm0 * ldc + cn0) * (int64_t)sizeof(Out),
+                ((M - 1 - cm0) * ldc + (N - cn0)) * (int64_t)sizeof(Out), ldc, N - cn0, wave, lane, acc);
           goto stored;
         }
       }

@@ -168,6 +168,9 @@ def test_plan_choices_for_the_workloads():
         assert (p.variant, p.bm, p.bn) == (tg.VARIANT_TILE, 128, 128)
         assert bool(p.flags & tg.FLAG_ROTATE_K) == (nn == 128)
         assert p.flags & tg.FLAG_PERSIST and not p.flags & tg.FLAG_PREFETCH  # HBM-bound: LDS-staged stores
+        assert p.flags & tg.FLAG_STREAM_C  # outputs of 128 MiB and 2 GiB: non-temporal stores
+        assert tg.plan_tile(p, tg.VARIANT_TILE, 1).flags & tg.FLAG_STREAM_C  # kept by a re-plan
+    assert not tg.plan(2048, 2048, 128, trans_b=True).flags & tg.FLAG_STREAM_C  # 16 MiB: stays cached
     with pytest.raises(tg.TgError):
         tg.plan(64, 64, 64, batch=0)
     p = tg.plan(8192, 8192, 8192, out_dtype=torch.bfloat16)

@@ -221,3 +221,22 @@ def test_persistent_launch_matches_one_workgroup_per_tile(ta, tb, out_dtype):
                 assert np.array_equal(outs[0][0], o[0]), what
             got = outs[0][1][idx[:, 0], idx[:, 1], idx[:, 2]]
             check(got, ref, t, out_dtype, what)
+
+
+@pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
+def test_non_temporal_c_stores_give_the_same_result(out_dtype):
+    """TG_FLAG_STREAM_C only changes the cache policy of the C stores."""
+    rng = np.random.default_rng(31)
+    m, n, k, batch = 264, 392, 200, 3
+    A = to_gpu(synth.draw(rng, (batch, m, k), "normal", 1.0))
+    B = to_gpu(synth.draw(rng, (batch, n, k), "normal", 1.0))
+    tout = torch_out_dtype(out_dtype)
+    outs = []
+    for flag in (0, 1):
+        p = tg.plan(m, n, k, trans_b=True, out_dtype=tout, batch=batch)
+        p.flags = (p.flags & ~tg.FLAG_STREAM_C) | (tg.FLAG_STREAM_C if flag else 0)
+        C = torch.empty((batch, m, n), dtype=tout, device="cuda")
+        tg.bmm_run(p, batch, m * k, n * k, m * n, A, B, C)
+        outs.append(C)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
