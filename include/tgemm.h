@@ -60,6 +60,17 @@ typedef enum {
   TG_VARIANT_SKINNY = 2   /* M <= 32, both operands K-contiguous: streams B once */
 } tg_variant;
 
+/* Entries of the TG_VARIANT_TILE table served by the ping-pong kernel: 8
+ * waves in two groups that take turns between a matrix-core phase and a
+ * memory phase (256 x 256 tiles, 64-deep K steps, three A and two B LDS
+ * buffers, so lds_bytes = (3*bm*bk + 2*bk*bn) * 2).  gemm_plan picks it for
+ * large MFMA-bound problems.  TG_TILE_PINGPONG_EPI is the same kernel with the
+ * alpha/beta/bias epilogue compiled in; the run calls use whichever of the two
+ * matches the call (with or without an epilogue), and the 8-wave tile kernel
+ * (entry 8) when K = 0. */
+#define TG_TILE_PINGPONG 23
+#define TG_TILE_PINGPONG_EPI 24
+
 /* plan.flags bits */
 #define TG_FLAG_EVEN_K 0x1 /* K is a multiple of the K-tile: no masked K step */
 #define TG_FLAG_VEC16 0x2  /* leading dims and contiguous extents allow 16-byte loads */

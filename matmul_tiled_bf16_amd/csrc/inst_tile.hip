@@ -8,6 +8,7 @@
 
 #include "tiles.hpp"
 #include "tile_gemm.hpp"
+#include "pingpong_gemm.hpp"
 #include "generic_gemm.hpp"
 
 
@@ -17,8 +18,13 @@ namespace {
 template <int T>
 constexpr KernelFn tile_k() {
   constexpr TileShape s = kTiles[T];
-  return &tile_gemm_kernel<TG_IN, TG_OUT, s.bm, s.bn, s.bk, s.wm, s.wn, s.stages, s.occ,
-                           s.dw ? s.dw : s.wm * s.wn, TG_TA != 0, TG_TB != 0>;
+  if constexpr (s.kind == kPingPong)
+    return &pingpong_gemm_kernel<TG_IN, TG_OUT, TG_TA != 0, TG_TB != 0, false>;
+  else if constexpr (s.kind == kPingPongEpi)
+    return &pingpong_gemm_kernel<TG_IN, TG_OUT, TG_TA != 0, TG_TB != 0, true>;
+  else
+    return &tile_gemm_kernel<TG_IN, TG_OUT, s.bm, s.bn, s.bk, s.wm, s.wn, s.stages, s.occ,
+                             s.dw ? s.dw : s.wm * s.wn, TG_TA != 0, TG_TB != 0>;
 }
 template <int T>
 constexpr KernelFn generic_k() {

@@ -1,0 +1,460 @@
+// pingpong_gemm.hpp -- gfx950 GEMM/BMM for large MFMA-bound products: eight
+// waves that alternate between a matrix-core phase and a memory phase.
+//
+// A work-group computes 256 x 256 tiles of C[b] = op(A[b]) op(B[b]) with
+// eight waves in two groups of four.  Wave w runs on SIMD w mod 4, so every
+// SIMD holds one wave of each group; a wave of group g owns rows
+// [128 g, 128 g + 128) and columns [64 s, 64 s + 64) of the tile (s = w mod 4).
+// The groups take turns, one work-group barrier per turn:
+//
+//   phase 2k   : group 0 reads its fragments of K step k from LDS (and
+//                issues the HBM->LDS copies of step k + 1); group 1 runs the
+//                MFMAs of step k - 1.
+//   phase 2k+1 : group 0 runs the MFMAs of step k; group 1 reads its
+//                fragments of step k.
+//
+// So on every SIMD one wave issues nothing but back-to-back MFMAs on
+// fragments already in its registers while the other wave waits on LDS and
+// HBM, and the matrix core idles only at the turn.  A turn's MFMAs (8 blocks
+// of 32 x 32, four 16-deep slices) outlast the other group's LDS reads.  This
+// is the pages' producer/consumer split ("FLA Triton -> Gluon Porting
+// Skill", section 5: warp-specialised pipelines) expressed with the two waves
+// that share a SIMD.
+//
+//  * Staging, swizzles, op() by addressing and the zero-filled tails are the
+//    tile kernel's (same LDS layout as DmaOperand and swz_off,
+//    ds_read_b64_tr_b16 for M/N-contiguous operands), with the addressing
+//    folded into a few registers: a wave holds 128 accumulators and 96
+//    fragment registers of 256.
+//  * Ring: two LDS buffers of one 64-deep K step (2 x 64 KiB).  Step k + 1
+//    goes into the buffer of step k - 1, which group 1 finished reading
+//    before the barrier that opens phase 2k.  Group 0 waits for its copies of
+//    step k + 1 at the end of its MFMA phase 2k+1, before the barrier that
+//    opens phase 2k+2, where it reads step k + 1.
+//  * Persistent: a work-group takes items blockIdx.x, blockIdx.x + gridDim.x,
+//    ... (the XCD-aware order of work_coords), and their K steps form one
+//    stream -- the copies of an item's first step are issued during the
+//    previous item's last step like any other.  Each group stores a finished
+//    item from registers at the start of its next memory phase, while the
+//    other group runs MFMAs; the first step of an item starts its MFMAs from
+//    zero accumulators.
+#pragma once
+
+#include "tile_gemm.hpp"
+
+namespace tg {
+
+// HBM->LDS copies of one operand's K step, issued by NW waves (the tile
+// kernel's DmaOperand layout and swizzle).  Instruction i of a wave lands
+// RPI tile rows below instruction i - 1, and the swizzle of its source units
+// depends on i only through i mod 2, so a wave's source offsets are two
+// per-lane values plus multiples of one uniform stride: two registers
+// instead of one per instruction.
+template <bool KC, int MN_T, int BK, int NW>
+struct DmaPair {
+  static constexpr int CH = KC ? BK / 8 : MN_T / 8;
+  static constexpr int BYTES = MN_T * BK * 2;
+  static constexpr int INSTR = BYTES / 1024;
+  static constexpr int IPW = INSTR / NW;
+  static constexpr int RPI = 1024 / (CH * 16);  // tile rows per instruction
+  static_assert(BYTES % 1024 == 0 && INSTR % NW == 0 && IPW % 2 == 0 && RPI >= 1, "whole 1 KiB wave loads, in pairs");
+
+  uint32_t vb[2];  // source byte offsets of instructions 0 and 1
+
+  static __device__ __forceinline__ uint32_t unit_of(int wave, int lane, int p, uint32_t& row) {
+    const uint32_t o = (uint32_t)(wave * IPW + p) * 1024u + 16u * lane;
+    row = o / (CH * 16);
+    return ((o / 16) % CH) ^ swz_unit<KC, CH>(row);
+  }
+  __device__ __forceinline__ void init(int wave, int lane, int64_t ld) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      uint32_t row;
+      const uint32_t unit = unit_of(wave, lane, p, row);
+      vb[p] = row * (uint32_t)ld * 2u + unit * 16u;
+    }
+  }
+  // keep the offsets in registers (the compiler would rather recompute them
+  // in the loop, which costs issue slots in the memory phase)
+  __device__ __forceinline__ void pin() { asm volatile("" : "+v"(vb[0]), "+v"(vb[1])); }
+
+  // base: element (mn0, k0) [KC] or (k0, mn0) [MN]; bytes: from base to the
+  // end of the matrix's last element; k_left = K - k0 (units at or past K
+  // of a K-contiguous tile read zero when MASK_K).
+  template <bool MASK_K>
+  __device__ __forceinline__ void issue(const uint16_t* base, int64_t bytes, int64_t ld, uint32_t tile_lds, int wave,
+                                        int lane, int64_t k_left) const {
+    const i32x4 rs = make_rsrc(base, bytes);
+    const uint32_t step2 = (uint32_t)(2 * RPI) * (uint32_t)ld * 2u;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      uint32_t off = vb[i & 1] + (uint32_t)(i >> 1) * step2;
+      if constexpr (MASK_K && KC) {
+        uint32_t row;
+        const uint32_t kofs = unit_of(wave, lane, i & 1, row) * 8;
+        off = (int64_t)kofs < k_left ? off : kOutOfRange;
+      }
+      dma16(rs, off, tile_lds + (uint32_t)(wave * IPW + i) * 1024u);
+    }
+  }
+};
+
+// LDS byte offsets of a wave's MFMA fragments: NB blocks of 32 rows (K-
+// contiguous tile) or 32 columns (M/N-contiguous tile) starting at mn0, for
+// each 16-deep slice ks of a stage.  K-contiguous rows hold 64 elements (CH
+// = 8 units): a block 32 rows down is 4 KiB further, and slice ks flips bits
+// 5-6 of the slice-0 offset (the swizzle XORs whole units), so one register
+// serves every fragment.  M/N-contiguous tiles keep one register per block;
+// a slice is 16 rows further.
+template <bool KC, int CH, int NB>
+struct FragAddr {
+  static_assert(!KC || CH == 8, "K-contiguous fragments need 64-element rows");
+  uint32_t r[KC ? 1 : NB];
+  __device__ __forceinline__ void init(int mn0, int lane) {
+    const int li = lane & 31, lg = lane >> 5, trh = lane >> 4, trs = lane & 15;
+    if constexpr (KC) {
+      r[0] = swz_off<true, CH>(mn0 + li, lg * 8);
+    } else {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        r[b] = swz_off<false, CH>(8 * (trh >> 1) + (trs >> 2), mn0 + 32 * b + 16 * (trh & 1) + 4 * (trs & 3));
+    }
+  }
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int b = 0; b < (KC ? 1 : NB); ++b) asm volatile("" : "+v"(r[b]));
+  }
+  __device__ __forceinline__ uint32_t at(int ks, int b) const {
+    if constexpr (KC)
+      return (r[0] ^ (uint32_t)(ks << 5)) + (uint32_t)b * 32u * CH * 16u;
+    else
+      return r[b] + (uint32_t)ks * 16u * CH * 16u;
+  }
+};
+
+// Vector store of a wave's FM x FN blocks of C (acc holds C^T: four
+// consecutive columns of one row per group of four registers), issued as
+// exactly FM * FN * 4 store instructions.  Column offsets inside the blocks
+// are instruction immediates; a tile that ends inside the blocks (n_left <
+// FN * 32) masks whole 4-column groups at or past n_left (the caller
+// guarantees N % 4 == 0).  Rows past the descriptor's end are dropped.
+// Each group is converted right before its store, so only two temporaries
+// are live besides the accumulators.
+template <typename Out, int FM, int FN>
+__device__ __forceinline__ void store_blocks_counted(const void* Ctile, int64_t bytes, int64_t ldc, int64_t n_left,
+                                                     int lane, const f32x16 (&acc)[FM][FN]) {
+  const __amdgpu_buffer_rsrc_t rs = store_rsrc(Ctile, bytes);
+  const int li = lane & 31, lg = lane >> 5;
+  constexpr uint32_t es = sizeof(Out);
+  const bool full = n_left >= FN * 32;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const uint32_t rowoff = (uint32_t)((i * 32 + li) * ldc) * es + 4u * lg * es;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t col = (uint32_t)(j * 32 + 8 * g);
+        const uint32_t off = (full || (int64_t)(col + 4 * lg) < n_left) ? rowoff + col * es : kOutOfRange;
+        const f32x16& a = acc[i][j];
+        if constexpr (es == 4) {
+          buf_store16(rs, off, __builtin_bit_cast(u32x4, f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]}));
+        } else {
+          buf_store8(rs, off, u32x2{pack2<Out>(a[4 * g], a[4 * g + 1]), pack2<Out>(a[4 * g + 2], a[4 * g + 3])});
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
+template <typename In, typename Out, bool TA, bool TB, bool EPI>
+__global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(GemmArgs args) {
+  constexpr int BM = 256, BN = 256, BK = 64, WN = 4;
+  constexpr int WTM = 128, WTN = 64, FM = WTM / 32, FN = WTN / 32, KS = BK / 16;
+  constexpr bool A_KC = !TA, B_KC = TB;
+  using OA = DmaPair<A_KC, BM, BK, 4>;  // issued by the four waves of group 1
+  using OB = DmaPair<B_KC, BN, BK, 4>;  // issued by the four waves of group 0
+  constexpr uint32_t A_BYTES = OA::BYTES, B_BYTES = OB::BYTES;
+  constexpr uint32_t B_BASE = 3 * A_BYTES;  // three A buffers, then two B buffers
+  constexpr int PA = OA::IPW, PB = OB::IPW;  // copy instructions per wave per step
+  constexpr int ST = FM * FN * 4;            // store instructions of store_blocks_counted
+  static_assert(B_BASE + 2 * B_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(PA + ST < 64 && PB + ST < 64, "counted waits fit the vector-memory counter");
+
+  extern __shared__ __attribute__((aligned(1024))) char tg_smem[];
+  TG_LDS char* lds = (TG_LDS char*)tg_smem;
+  const uint32_t lds0 = (uint32_t)(size_t)lds;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave / WN, sw = wave % WN;
+  const int wm0 = grp * WTM, wn0 = sw * WTN;
+
+  const int64_t M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb, ldc = args.ldc;
+  const int64_t total = (int64_t)args.tiles_m * args.tiles_n * args.batch;
+  if ((int64_t)blockIdx.x >= total || K <= 0) return;  // (the launcher never sends K = 0 here)
+  // This work-group's items are blockIdx.x, blockIdx.x + gridDim.x, ...; their
+  // K steps form one stream of nsteps steps.
+  const int64_t nk = (K + BK - 1) / BK;
+  const int64_t items = (total - 1 - (int64_t)blockIdx.x) / gridDim.x + 1;
+  const int64_t nsteps = items * nk;
+
+  struct Item {
+    int64_t b, m0, n0;
+  };
+  // item t of this work-group: work_coords' XCD-aware order in 32-bit
+  // arithmetic (the launcher keeps total below 2^31)
+  auto item_of = [&](int64_t t) {
+    const uint32_t tot = (uint32_t)total, tm = (uint32_t)args.tiles_m, tn = (uint32_t)args.tiles_n;
+    const uint32_t w0 = blockIdx.x + (uint32_t)t * gridDim.x;
+    const uint32_t per = tot >> 3, rem = tot & 7, x = w0 & 7, local = w0 >> 3;
+    const uint32_t id = x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
+    const uint32_t G = tm * tn, bb = id / G, tt = id - bb * G;
+    const uint32_t band = 8 * tn, bidx = tt / band, first_m = bidx * 8;
+    const uint32_t gsz = min(tm - first_m, 8u), in_band = tt - bidx * band;
+    Item it;
+    it.b = bb;
+    it.m0 = (int64_t)(first_m + in_band % gsz) * BM;
+    it.n0 = (int64_t)(in_band / gsz) * BN;
+    return it;
+  };
+
+  // Copy cursor of one operand: the next step it copies, as (item, step in
+  // item), with that item's panel base and remaining bytes.
+  struct Cursor {
+    int64_t t, k;
+    const char* base;
+    int64_t left0;
+  };
+  auto a_seek = [&](Cursor& c) {
+    const Item it = item_of(c.t);
+    c.base = (const char*)(args.A + it.b * args.sA + (A_KC ? it.m0 * lda : it.m0));
+    c.left0 = A_KC ? ((M - 1 - it.m0) * lda + K) * 2 : ((K - 1) * lda + (M - it.m0)) * 2;
+  };
+  auto b_seek = [&](Cursor& c) {
+    const Item it = item_of(c.t);
+    c.base = (const char*)(args.B + it.b * args.sB + (B_KC ? it.n0 * ldb : it.n0));
+    c.left0 = B_KC ? ((N - 1 - it.n0) * ldb + K) * 2 : ((K - 1) * ldb + (N - it.n0)) * 2;
+  };
+  const int64_t a_step = A_KC ? (int64_t)BK * 2 : (int64_t)BK * lda * 2;
+  const int64_t b_step = B_KC ? (int64_t)BK * 2 : (int64_t)BK * ldb * 2;
+  OA oa;
+  OB ob;
+  oa.init(sw, lane, lda);
+  ob.init(sw, lane, ldb);
+  // copy the cursor's step into buffer `buf`, then advance the cursor
+  auto copy_a = [&](Cursor& c, uint32_t buf) {
+    const int64_t k_left = K - c.k * BK, off = c.k * a_step;
+    const uint32_t dst = lds0 + buf * A_BYTES;
+    if (k_left >= BK)
+      oa.template issue<false>((const uint16_t*)(c.base + off), c.left0 - off, lda, dst, sw, lane, k_left);
+    else
+      oa.template issue<true>((const uint16_t*)(c.base + off), c.left0 - off, lda, dst, sw, lane, k_left);
+    if (++c.k == nk) {
+      c.k = 0;
+      if (++c.t < items) a_seek(c);
+    }
+  };
+  auto copy_b = [&](Cursor& c, uint32_t buf) {
+    const int64_t k_left = K - c.k * BK, off = c.k * b_step;
+    const uint32_t dst = lds0 + B_BASE + buf * B_BYTES;
+    if (k_left >= BK)
+      ob.template issue<false>((const uint16_t*)(c.base + off), c.left0 - off, ldb, dst, sw, lane, k_left);
+    else
+      ob.template issue<true>((const uint16_t*)(c.base + off), c.left0 - off, ldb, dst, sw, lane, k_left);
+    if (++c.k == nk) {
+      c.k = 0;
+      if (++c.t < items) b_seek(c);
+    }
+  };
+
+  // LDS byte offsets of this wave's fragment reads
+  FragAddr<A_KC, OA::CH, FM> fra;
+  FragAddr<B_KC, OB::CH, FN> frb;
+  fra.init(wm0, lane);
+  frb.init(wn0, lane);
+  constexpr uint32_t A_TR4 = 4 * OA::CH * 16, B_TR4 = 4 * OB::CH * 16;
+
+  f32x16 acc[FM][FN];
+  u32x4 fa[KS][FM], fb[KS][FN];
+
+  // memory phase: this wave's fragments of every slice of the step held in
+  // A buffer abuf and B buffer bbuf
+  auto mem = [&](uint32_t abuf, uint32_t bbuf) {
+    const TG_LDS char* sa = lds + abuf * A_BYTES;
+    const TG_LDS char* sb = lds + B_BASE + bbuf * B_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (A_KC) {
+          fa[ks][i] = lds_read16(sa, fra.at(ks, i));
+        } else {
+          const u32x2 lo = lds_read_tr(sa, fra.at(ks, i)), hi = lds_read_tr(sa, fra.at(ks, i) + A_TR4);
+          fa[ks][i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (B_KC) {
+          fb[ks][j] = lds_read16(sb, frb.at(ks, j));
+        } else {
+          const u32x2 lo = lds_read_tr(sb, frb.at(ks, j)), hi = lds_read_tr(sb, frb.at(ks, j) + B_TR4);
+          fb[ks][j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+      }
+    }
+  };
+  // MFMA phase: snake order over the blocks, so consecutive MFMAs share an
+  // operand; the first step of an item starts from zero accumulators
+  auto comp = [&](auto first) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj) {
+          const int j = (i & 1) ? FN - 1 - jj : jj;
+          if (decltype(first)::value && ks == 0)
+            acc[i][j] = mfma32<In>(fb[ks][j], fa[ks][i], f32x16{});
+          else
+            acc[i][j] = mfma32<In>(fb[ks][j], fa[ks][i], acc[i][j]);
+        }
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    block_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Stores of item t's result (in acc).  A persistent launch (no epilogue,
+  // N % 4 == 0, checked by the launcher) stores each finished item inside
+  // the loop and every wave issues exactly ST vector stores -- a wave
+  // outside C stores through an empty descriptor, which drops every access
+  // -- because the counted waits allow exactly ST.  Otherwise the one item
+  // is stored after the loop, with the epilogue and the element-wise path
+  // for any N.
+  const bool persistent = !EPI && (int64_t)gridDim.x < total;
+  auto store_counted = [&](int64_t t) {
+    const Item it = item_of(t);
+    char* Cb = (char*)args.C + it.b * args.sC * (int64_t)sizeof(Out);
+    const int64_t r0 = it.m0 + wm0, c0 = it.n0 + wn0;
+    const bool in = r0 < M && c0 < N;
+    store_blocks_counted<Out, FM, FN>(in ? Cb + (r0 * ldc + c0) * (int64_t)sizeof(Out) : Cb,
+                                      in ? ((M - 1 - r0) * ldc + (N - c0)) * (int64_t)sizeof(Out) : 0, ldc,
+                                      in ? N - c0 : 0, lane, acc);
+  };
+  auto store_final = [&](int64_t t) {
+    const Item it = item_of(t);
+    char* Cb = (char*)args.C + it.b * args.sC * (int64_t)sizeof(Out);
+    const int64_t r0 = it.m0 + wm0, c0 = it.n0 + wn0;
+    if (r0 >= M || c0 >= N) return;
+    if (N % 4 == 0 || it.n0 + BN <= N) {
+      char* Ct = Cb + (r0 * ldc + c0) * (int64_t)sizeof(Out);
+      const int64_t bytes = ((M - 1 - r0) * ldc + (N - c0)) * (int64_t)sizeof(Out);
+      if constexpr (EPI) epilogue_acc_vec<Out, FM, FN>(args, Ct, bytes, ldc, N - c0, c0, lane, acc);
+      store_tile_vec<Out, FM, FN>(Ct, bytes, ldc, N - c0, lane, acc);
+    } else {
+      if constexpr (EPI) epilogue_acc<Out, FM, FN>(args, Cb, ldc, M, N, r0, c0, lane, acc);
+      store_tile<Out, FM, FN>(Cb, ldc, M, N, r0, c0, lane, acc);
+    }
+  };
+
+  // Copy schedule (global step g; A in buffer g mod 3, B in buffer g mod 2):
+  //  * prologue, group 0: A(0), B(0), A(1);
+  //  * group 0's memory phase of step g: B(g + 1), into the buffer of step
+  //    g - 1, which group 1 read in the previous phase; group 0 waits for it
+  //    at the end of its MFMA phase, before the barrier after which it reads
+  //    step g + 1;
+  //  * group 1's memory phase of step g: A(g + 2), into the buffer of step
+  //    g - 1; group 1 waits for A(g + 1) (its own copy of the previous
+  //    phase, or group 0's prologue copy) at the end of this memory phase,
+  //    before the barrier after which group 0 reads step g + 1.
+  // Both groups move 32 KiB per step into LDS besides their 96 KiB of
+  // fragment reads, so the two memory phases carry equal LDS traffic.
+  Cursor cur{0, 0, nullptr, 0};
+  if (grp == 0) {
+    Cursor ca{0, 0, nullptr, 0};
+    a_seek(ca);
+    b_seek(cur);
+    copy_a(ca, 0);
+    copy_b(cur, 0);
+    if (nsteps > 1) {
+      copy_a(ca, 1);
+      wait_vmcnt<PA, true>();  // A(0) and B(0) have landed; A(1) may not have
+    } else {
+      wait_vmcnt<0, true>();
+    }
+  } else {
+    // group 1's cursor starts at A(2)
+    cur.t = 2 / nk;
+    cur.k = 2 - cur.t * nk;
+    if (cur.t < items) a_seek(cur);
+  }
+  barrier();
+  if (grp == 1) barrier();  // group 1 runs one phase behind
+
+  int64_t kk = 0, t = 0;  // step within the item, item
+  uint32_t abuf = 0, bbuf = 0;  // buffers of step g
+  for (int64_t g = 0; g < nsteps; ++g) {
+    fra.pin();
+    frb.pin();
+    oa.pin();
+    ob.pin();
+    // memory phase: this group's copies, the previous item's stores (after
+    // the copies, so that the waits may leave them in flight), then the
+    // fragments of step g
+    const bool stored = !EPI && kk == 0 && g > 0;
+    bool copied = false;
+    if (grp == 0) {
+      if (g + 1 < nsteps) {
+        copy_b(cur, bbuf ^ 1u);
+        copied = true;
+      }
+    } else if (g + 2 < nsteps) {
+      copy_a(cur, abuf == 0 ? 2u : abuf - 1);
+      copied = true;
+    }
+    if constexpr (!EPI) {
+      if (stored) store_counted(t - 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mem(abuf, bbuf);
+    if (grp == 1) {
+      // A(g + 1) has landed; A(g + 2) and the stores may still be in flight
+      if (copied) {
+        if (stored) wait_vmcnt<PA + ST, true>();
+        else wait_vmcnt<PA, true>();
+      } else {
+        if (stored) wait_vmcnt<ST, true>();
+        else wait_vmcnt<0, true>();
+      }
+    } else {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers
+    }
+    barrier();
+    if (kk == 0)
+      comp(std::true_type{});
+    else
+      comp(std::false_type{});
+    if (grp == 0 && copied) {
+      // B(g + 1) has landed; the stores issued after it may not have
+      if (stored) wait_vmcnt<ST, false>();
+      else wait_vmcnt<0, false>();
+    }
+    if (grp == 0 || g + 1 < nsteps) barrier();
+    abuf = abuf == 2 ? 0u : abuf + 1;
+    bbuf ^= 1u;
+    if (++kk == nk) {
+      kk = 0;
+      ++t;
+    }
+  }
+  if (persistent)
+    store_counted(items - 1);
+  else
+    store_final(items - 1);
+}
+
+}  // namespace tg

@@ -95,7 +95,8 @@ int skinny_choose(int64_t m, int64_t) { return m > 16 ? 1 : 0; }
 // Step 1 roofline classification and shape-specific tuning; a small M wants a
 // small BLOCK_M).  Work items are tiles times batch matrices.
 //  * MFMA-bound problems (arithmetic intensity above MI355X's ~312 FLOP/B
-//    ridge) take the 256x256 8-wave tile when there are >= 2 items per CU;
+//    ridge) take the 256x256 ping-pong kernel (8 waves alternating MFMA and
+//    memory phases) when there are >= 2 items per CU;
 //  * HBM-bound ones take 128x128 tiles, two work-groups per CU, whose
 //    operand panels and 1 KiB row-segment stores keep the streams long;
 //  * small and ragged problems take smaller tiles so that there are at least
@@ -106,7 +107,7 @@ int choose_tile(int64_t m, int64_t n, int64_t k, int64_t batch, int out_size) {
   const double flops = 2.0 * (double)m * (double)n * (double)k;
   const double bytes = 2.0 * ((double)m * k + (double)k * n) + (double)out_size * m * n;
   const bool mfma_bound = bytes > 0 && flops / bytes > 312.5;
-  if (mfma_bound && items(8) >= 512) return 8;  // 256x256, 8 waves
+  if (mfma_bound && items(8) >= 512 && k > 0) return tg::kPingPongTile;  // 256x256, 8 waves
   if (items(13) >= 256) return mfma_bound ? 1 : 13;  // 128x128
   return 0;                                          // 64x64
 }
@@ -342,6 +343,17 @@ static tg_status launch(const gemm_plan_t* plan, const gemm_epilogue_t* epi, int
   a.stream_c = (variant == TG_VARIANT_TILE && (p.flags & TG_FLAG_STREAM_C)) ? 1 : 0;
   if (a.epi && a.bias && (uintptr_t)a.bias % (p.out_type == TG_FP32 ? 4 : 2) != 0) return TG_ERR_INVALID;
 
+  // The ping-pong kernel: its epilogue entry when there is an epilogue; the
+  // 8-wave tile kernel for K = 0 (which it does not handle) and for more
+  // items than its 32-bit item order covers.
+  const bool pingpong = variant == TG_VARIANT_TILE && kTiles[tile].kind != tg::kTileKernel;
+  if (pingpong) {
+    const int64_t items = cdiv(p.m, kTiles[tile].bm) * cdiv(p.n, kTiles[tile].bn) * batch;
+    if (p.k == 0 || items >= ((int64_t)1 << 30))
+      tile = 8;
+    else
+      tile = a.epi ? tg::kPingPongEpiTile : tg::kPingPongTile;
+  }
   const Launch l = launch_shape(variant, tile);
   const int io = p.in_type == TG_BF16 ? 0 : 1, oo = p.out_type == TG_FP32 ? 0 : 1;
   KernelFn fn;
@@ -366,7 +378,12 @@ static tg_status launch(const gemm_plan_t* plan, const gemm_epilogue_t* epi, int
     // keeps every item on the XCD the kernel's tile order assumes)
     const int64_t total = groups * batch;
     int64_t cap = (int64_t)1 << 30;
-    if (variant == TG_VARIANT_TILE && (p.flags & TG_FLAG_PERSIST) && !a.epi) {
+    if (variant == TG_VARIANT_TILE && kTiles[tile].kind == tg::kPingPong) {
+      // persistent ping-pong: one work-group per CU; it stores each finished
+      // tile with 4-column vector stores (N % 4 == 0) and has no epilogue
+      const int64_t slots = (int64_t)compute_units();
+      if ((p.flags & TG_FLAG_PERSIST) && p.n % 4 == 0 && slots > 0 && total >= 2 * slots) cap = slots;
+    } else if (variant == TG_VARIANT_TILE && (p.flags & TG_FLAG_PERSIST) && !a.epi) {
       // persistent: one work-group per resident slot (a multiple of 8)
       const int64_t slots = (int64_t)compute_units() * kTiles[tile].occ;
       if (slots > 0 && total >= 2 * slots) {

@@ -686,7 +686,7 @@ __device__ __forceinline__ void tile_gemm_body(const KA& kargs) {
       int d = 0;
 #pragma unroll
       for (int m = 0; m < MMAS; ++m) {
-        const int i = m / FN, j = m % FN;
+        const int i = m / FN, j = (i & 1) ? FN - 1 - m % FN : m % FN;  // snake order
         acc[i][j] = mfma32<In>(cur.b[j], cur.a[i], acc[i][j]);
         if (nxt && m < READS) read_one(nbase, nks, m, *nxt);
         if (rsa && m % every == every - 1 && d < cnt) {
@@ -709,7 +709,10 @@ __device__ __forceinline__ void tile_gemm_body(const KA& kargs) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<In>(f.b[j], f.a[i], acc[i][j]);
+        for (int jj = 0; jj < FN; ++jj) {
+          const int j = (i & 1) ? FN - 1 - jj : jj;  // snake order
+          acc[i][j] = mfma32<In>(f.b[j], f.a[i], acc[i][j]);
+        }
     };
 
     if (nk > 0) {

@@ -9,10 +9,18 @@
 
 namespace tg {
 
+// Kernel behind a tile entry.
+enum TileKind {
+  kTileKernel = 0,  // tile_gemm_kernel (tile_gemm.hpp)
+  kPingPong = 1,    // pingpong_gemm_kernel without epilogue: persistent when there is enough work
+  kPingPongEpi = 2  // pingpong_gemm_kernel with the alpha/beta/bias epilogue (one tile per work-group)
+};
+
 struct TileShape {
   int bm, bn, bk, wm, wn, stages;
   int occ = 1;  // work-groups meant to share one CU (register/LDS budget per wave follows)
   int dw = 0;   // waves that issue the HBM->LDS copies (0: all of them)
+  int kind = kTileKernel;
 };
 
 constexpr TileShape kTiles[] = {
@@ -47,7 +55,13 @@ constexpr TileShape kTiles[] = {
     // 8 waves, 4 of them copy: persistent work-groups whose copy waves
     // prefetch while the other waves store (split mode)
     {128, 128, 64, 2, 4, 2, 2, 4},  // 22: 64x32 per wave, 64 KiB
+    // 8 waves in two groups that alternate MFMA and memory phases
+    // (pingpong_gemm.hpp): 128x64 per wave, 64-deep K steps, three A and two
+    // B LDS buffers (160 KiB); the second entry adds the epilogue
+    {256, 256, 64, 2, 4, 2, 1, 4, kPingPong},     // 23
+    {256, 256, 64, 2, 4, 2, 1, 4, kPingPongEpi},  // 24
 };
+constexpr int kPingPongTile = 23, kPingPongEpiTile = 24;
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 // Tiles a grouped launch may take (indices into kTiles): small and ragged
@@ -63,7 +77,9 @@ constexpr TileShape kGenericTiles[] = {
 };
 constexpr int kNumGeneric = sizeof(kGenericTiles) / sizeof(kGenericTiles[0]);
 
-constexpr int lds_bytes_of(const TileShape& t) { return t.stages * (t.bm * t.bk + t.bk * t.bn) * 2; }
+constexpr int lds_bytes_of(const TileShape& t) {
+  return t.kind != kTileKernel ? (3 * t.bm * t.bk + 2 * t.bk * t.bn) * 2 : t.stages * (t.bm * t.bk + t.bk * t.bn) * 2;
+}
 
 // Whether the tile kernel can run persistently: the first wait of a
 // prefetched item counts the copy instructions of the stages after the first
@@ -73,6 +89,7 @@ constexpr int lds_bytes_of(const TileShape& t) { return t.stages * (t.bm * t.bk 
 // size: dedicated copy waves, a C tile that fits the ring's LDS in one band,
 // and a band that divides evenly over the waves that store it.
 constexpr bool split_ok(const TileShape& t, int out_size) {
+  if (t.kind != kTileKernel) return false;
   const int nw = t.wm * t.wn;
   const int stores = nw - (t.dw ? t.dw : nw);
   const int c_bytes = t.bm * t.bn * out_size;
@@ -81,6 +98,7 @@ constexpr bool split_ok(const TileShape& t, int out_size) {
 }
 
 constexpr bool persist_ok(const TileShape& t) {
+  if (t.kind != kTileKernel) return false;
   const int copy_waves = t.dw ? t.dw : t.wm * t.wn;
   const int per_step = (t.bm * t.bk * 2 / 1024) / copy_waves + (t.bk * t.bn * 2 / 1024) / copy_waves;
   const int d = t.stages >= 3 ? t.stages - 1 : t.stages;

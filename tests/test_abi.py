@@ -190,7 +190,10 @@ def test_lds_budget_matches_the_staging_formula_and_fits():
     for m, n, k in [(256, 256, 256), (1000, 1000, 1000), (8192, 8192, 8192), (2048, 128, 2048), (17, 33, 63)]:
         st, p = raw_plan(m=m, n=n, k=k)
         assert st == tg.TG_OK
-        if p.variant != tg.VARIANT_SKINNY:
+        if p.variant == tg.VARIANT_TILE and p.tile in (tg.TILE_PINGPONG, tg.TILE_PINGPONG_EPI):
+            # three A and two B buffers of one K step
+            assert p.lds_bytes == (3 * p.bm * p.bk + 2 * p.bk * p.bn) * 2
+        elif p.variant != tg.VARIANT_SKINNY:
             assert p.lds_bytes == roofline.lds_budget(p.bm, p.bn, p.bk, p.stages)
         assert p.lds_bytes <= roofline.MI355X_LDS_PER_WORKGROUP
 
@@ -318,3 +321,14 @@ def test_page_figures_pin_the_roofline_arithmetic():
     # the same arithmetic on MI355X: the 8192^3 GEMM is MFMA-bound, the M=16 one HBM-bound
     assert roofline.bound(8192, 8192, 8192, out_size=2) == "mfma"
     assert roofline.bound(16, 8192, 8192, out_size=2) == "hbm"
+
+
+def test_python_constants_match_the_header():
+    """The binding's copies of the header's tile and flag numbers."""
+    import re
+    text = open(tg.HEADER).read()
+    defs = dict(re.findall(r"#define\s+(TG_\w+)\s+(0x[0-9a-fA-F]+|\d+)", text))
+    assert int(defs["TG_TILE_PINGPONG"], 0) == tg.TILE_PINGPONG
+    assert int(defs["TG_TILE_PINGPONG_EPI"], 0) == tg.TILE_PINGPONG_EPI
+    for name in ("EVEN_K", "VEC16", "ROTATE_K", "PERSIST", "PREFETCH", "STREAM_C"):
+        assert int(defs["TG_FLAG_" + name], 0) == getattr(tg, "FLAG_" + name)
