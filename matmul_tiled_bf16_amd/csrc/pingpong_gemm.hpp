@@ -15,17 +15,21 @@
 //
 // So on every SIMD one wave issues nothing but back-to-back MFMAs on
 // fragments already in its registers while the other wave waits on LDS and
-// HBM, and the matrix core idles only at the turn.  A turn's MFMAs (8 blocks
-// of 32 x 32, four 16-deep slices) outlast the other group's LDS reads.  This
+// HBM, and the matrix core idles only at the turn.  A turn's MFMAs (32
+// blocks of 16 x 16, two 32-deep slices) outlast the other group's LDS reads.  This
 // is the pages' producer/consumer split ("FLA Triton -> Gluon Porting
 // Skill", section 5: warp-specialised pipelines) expressed with the two waves
 // that share a SIMD.
 //
-//  * Staging, swizzles, op() by addressing and the zero-filled tails are the
-//    tile kernel's (same LDS layout as DmaOperand and swz_off,
-//    ds_read_b64_tr_b16 for M/N-contiguous operands), with the addressing
-//    folded into a few registers: a wave holds 128 accumulators and 96
-//    fragment registers of 256.
+//  * v_mfma_f32_16x16x32: measured under the power cap on random bf16
+//    operands, it sustains ~7% more throughput than the 32x32x16 form (it
+//    moves half the accumulator data per flop).
+//  * Staging, op() by addressing and the zero-filled tails are the tile
+//    kernel's (direct-to-LDS copies, ds_read_b64_tr_b16 for M/N-contiguous
+//    operands), with a swizzle for M/N-contiguous tiles that suits the
+//    16x16x32 transposing reads, and the addressing folded into a few
+//    registers: a wave holds 128 accumulators and 96 fragment registers of
+//    256.
 //  * Ring: two LDS buffers of one 64-deep K step (2 x 64 KiB).  Step k + 1
 //    goes into the buffer of step k - 1, which group 1 finished reading
 //    before the barrier that opens phase 2k.  Group 0 waits for its copies of
@@ -44,12 +48,31 @@
 
 namespace tg {
 
-// HBM->LDS copies of one operand's K step, issued by NW waves (the tile
-// kernel's DmaOperand layout and swizzle).  Instruction i of a wave lands
+// LDS swizzle of the ping-pong kernel, in 16-byte units.  K-contiguous tiles
+// (rows of 64 elements) use the tile kernel's (row / 2) mod 8.  M/N-
+// contiguous tiles (rows along K, 256 elements) flip the unit index by
+// 2 * (bits 0-1 of the row, plus bit 3 of the row as bit 2): the transposing
+// reads of the 16x16x32 fragments put rows k..k+3 and k+8..k+11 in one LDS
+// clock, and these eight rows then land on eight distinct unit pairs.
+template <bool KC, int CH>
+__device__ __forceinline__ uint32_t pp_swz(uint32_t row) {
+  if constexpr (KC)
+    return swz_unit<true, CH>(row);
+  else
+    return (2u * ((row & 3u) | ((row >> 1) & 4u))) & (uint32_t)(CH - 1);
+}
+template <bool KC, int CH>
+__device__ __forceinline__ uint32_t pp_off(uint32_t row, uint32_t col) {
+  return row * (CH * 16u) + (((col >> 3) ^ pp_swz<KC, CH>(row)) << 4) + ((col & 7u) << 1);
+}
+
+// HBM->LDS copies of one operand's K step, issued by NW waves: lane t of a
+// wave's instruction i writes LDS bytes (wave * IPW + i) KiB + 16 t, and
+// fetches the source unit that the swizzle puts there.  Instruction i lands
 // RPI tile rows below instruction i - 1, and the swizzle of its source units
-// depends on i only through i mod 2, so a wave's source offsets are two
-// per-lane values plus multiples of one uniform stride: two registers
-// instead of one per instruction.
+// depends on i only through the bits in BMASK, so a wave's source offsets
+// are a few per-lane bases plus multiples of one uniform row stride (two or
+// four registers instead of one per instruction).
 template <bool KC, int MN_T, int BK, int NW>
 struct DmaPair {
   static constexpr int CH = KC ? BK / 8 : MN_T / 8;
@@ -57,26 +80,37 @@ struct DmaPair {
   static constexpr int INSTR = BYTES / 1024;
   static constexpr int IPW = INSTR / NW;
   static constexpr int RPI = 1024 / (CH * 16);  // tile rows per instruction
-  static_assert(BYTES % 1024 == 0 && INSTR % NW == 0 && IPW % 2 == 0 && RPI >= 1, "whole 1 KiB wave loads, in pairs");
+  // K-contiguous: the swizzle sees (row / 2) mod 8, i.e. instruction parity;
+  // M/N-contiguous (two rows per instruction): row bits 1 and 3, i.e.
+  // instruction bits 0 and 2
+  static constexpr int BMASK = KC ? 1 : 5;
+  static constexpr int NB = KC ? 2 : 4;
+  static_assert(KC ? CH == 8 : CH == 32, "64-deep K-contiguous rows or 256-wide M/N-contiguous rows");
+  static_assert(BYTES % 1024 == 0 && INSTR % NW == 0 && IPW % 8 == 0, "whole 1 KiB wave loads");
 
-  uint32_t vb[2];  // source byte offsets of instructions 0 and 1
+  uint32_t vb[NB];  // source byte offsets of the base instructions
 
-  static __device__ __forceinline__ uint32_t unit_of(int wave, int lane, int p, uint32_t& row) {
-    const uint32_t o = (uint32_t)(wave * IPW + p) * 1024u + 16u * lane;
+  static __device__ __forceinline__ int slot(int i) { return KC ? (i & 1) : ((i & 1) | ((i >> 1) & 2)); }
+  static __device__ __forceinline__ uint32_t unit_of(int wave, int lane, int i, uint32_t& row) {
+    const uint32_t o = (uint32_t)(wave * IPW + i) * 1024u + 16u * lane;
     row = o / (CH * 16);
-    return ((o / 16) % CH) ^ swz_unit<KC, CH>(row);
+    return ((o / 16) % CH) ^ pp_swz<KC, CH>(row);
   }
   __device__ __forceinline__ void init(int wave, int lane, int64_t ld) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int i = 0; i < 8; ++i) {
+      if ((i & BMASK) != i) continue;
       uint32_t row;
-      const uint32_t unit = unit_of(wave, lane, p, row);
-      vb[p] = row * (uint32_t)ld * 2u + unit * 16u;
+      const uint32_t unit = unit_of(wave, lane, i, row);
+      vb[slot(i)] = row * (uint32_t)ld * 2u + unit * 16u;
     }
   }
-  // keep the offsets in registers (the compiler would rather recompute them
+  // keep the bases in registers (the compiler would rather recompute them
   // in the loop, which costs issue slots in the memory phase)
-  __device__ __forceinline__ void pin() { asm volatile("" : "+v"(vb[0]), "+v"(vb[1])); }
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) asm volatile("" : "+v"(vb[b]));
+  }
 
   // base: element (mn0, k0) [KC] or (k0, mn0) [MN]; bytes: from base to the
   // end of the matrix's last element; k_left = K - k0 (units at or past K
@@ -85,100 +119,149 @@ struct DmaPair {
   __device__ __forceinline__ void issue(const uint16_t* base, int64_t bytes, int64_t ld, uint32_t tile_lds, int wave,
                                         int lane, int64_t k_left) const {
     const i32x4 rs = make_rsrc(base, bytes);
-    const uint32_t step2 = (uint32_t)(2 * RPI) * (uint32_t)ld * 2u;
+    const uint32_t row_bytes = (uint32_t)RPI * (uint32_t)ld * 2u;
+    const int32_t kl = k_left < BK ? (int32_t)k_left : BK;
+    uint32_t ln = lane;
+    if constexpr (MASK_K && KC) asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));  // (not hoisted)
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      uint32_t off = vb[i & 1] + (uint32_t)(i >> 1) * step2;
+      const int bi = i & BMASK;
+      uint32_t off = vb[slot(bi)] + (uint32_t)(i - bi) * row_bytes;
       if constexpr (MASK_K && KC) {
         uint32_t row;
-        const uint32_t kofs = unit_of(wave, lane, i & 1, row) * 8;
-        off = (int64_t)kofs < k_left ? off : kOutOfRange;
+        const uint32_t kofs = unit_of(wave, ln, i, row) * 8;
+        off = (int32_t)kofs < kl ? off : kOutOfRange;
       }
       dma16(rs, off, tile_lds + (uint32_t)(wave * IPW + i) * 1024u);
     }
   }
 };
 
-// LDS byte offsets of a wave's MFMA fragments: NB blocks of 32 rows (K-
-// contiguous tile) or 32 columns (M/N-contiguous tile) starting at mn0, for
-// each 16-deep slice ks of a stage.  K-contiguous rows hold 64 elements (CH
-// = 8 units): a block 32 rows down is 4 KiB further, and slice ks flips bits
-// 5-6 of the slice-0 offset (the swizzle XORs whole units), so one register
-// serves every fragment.  M/N-contiguous tiles keep one register per block;
-// a slice is 16 rows further.
-template <bool KC, int CH, int NB>
+// LDS byte offsets of a wave's 16x16x32 MFMA fragments: lane l supplies
+// row/column (l & 15) of a 16-wide block and the 8 consecutive k at
+// 8 (l >> 4) of a 32-deep slice.  K-contiguous tiles (rows of 64 elements,
+// CH = 8): a block 16 rows down is 2 KiB further, and slice ks flips bit 6
+// of the slice-0 offset (the swizzle XORs whole units).  M/N-contiguous
+// tiles (rows of 256 elements, CH = 32) are read with two transposing reads
+// of 4 k-rows each: a block 16 columns over flips bits 5-6, a slice is 32
+// rows (16 KiB) further and the second read 4 rows (2 KiB).  So one
+// register serves every fragment of an operand.
+template <bool KC, int CH>
 struct FragAddr {
-  static_assert(!KC || CH == 8, "K-contiguous fragments need 64-element rows");
-  uint32_t r[KC ? 1 : NB];
+  uint32_t r;
   __device__ __forceinline__ void init(int mn0, int lane) {
-    const int li = lane & 31, lg = lane >> 5, trh = lane >> 4, trs = lane & 15;
-    if constexpr (KC) {
-      r[0] = swz_off<true, CH>(mn0 + li, lg * 8);
-    } else {
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-        r[b] = swz_off<false, CH>(8 * (trh >> 1) + (trs >> 2), mn0 + 32 * b + 16 * (trh & 1) + 4 * (trs & 3));
-    }
+    const int i = lane & 15, h = lane >> 4;
+    if constexpr (KC)
+      r = pp_off<true, CH>(mn0 + i, 8 * h);
+    else
+      r = pp_off<false, CH>(8 * h + (i >> 2), mn0 + 4 * (i & 3));
   }
-  __device__ __forceinline__ void pin() {
-#pragma unroll
-    for (int b = 0; b < (KC ? 1 : NB); ++b) asm volatile("" : "+v"(r[b]));
-  }
+  __device__ __forceinline__ void pin() { asm volatile("" : "+v"(r)); }
   __device__ __forceinline__ uint32_t at(int ks, int b) const {
     if constexpr (KC)
-      return (r[0] ^ (uint32_t)(ks << 5)) + (uint32_t)b * 32u * CH * 16u;
+      return (r ^ (uint32_t)(ks << 6)) + (uint32_t)b * 16u * CH * 16u;
     else
-      return r[b] + (uint32_t)ks * 16u * CH * 16u;
+      return (r ^ (uint32_t)(b << 5)) + (uint32_t)ks * 32u * CH * 16u;
   }
+  static constexpr uint32_t TR4 = 4u * CH * 16u;  // second transposing read: 4 rows down
 };
 
-// Vector store of a wave's FM x FN blocks of C (acc holds C^T: four
-// consecutive columns of one row per group of four registers), issued as
-// exactly FM * FN * 4 store instructions.  Column offsets inside the blocks
-// are instruction immediates; a tile that ends inside the blocks (n_left <
-// FN * 32) masks whole 4-column groups at or past n_left (the caller
-// guarantees N % 4 == 0).  Rows past the descriptor's end are dropped.
-// Each group is converted right before its store, so only two temporaries
-// are live besides the accumulators.
+// A wave's result is FM x FN blocks of 16 x 16 (v_mfma_f32_16x16x32 with the
+// B fragment as the first operand): register q of block (i, j) of lane l is
+// C[16 i + (l & 15)][16 j + 4 (l >> 4) + q] relative to the wave's corner --
+// four consecutive columns of one row.
+
+// Vector store of the blocks, exactly FM * FN store instructions.  Column
+// offsets inside the wave's tile are instruction immediates; when the tile
+// ends inside the blocks (n_left < FN * 16) whole 4-column groups at or past
+// n_left are dropped (the caller guarantees N % 4 == 0 or a tile that ends
+// inside N).  Rows past the descriptor's end are dropped.  Each group is
+// converted right before its store, so only two temporaries are live
+// besides the accumulators.
 template <typename Out, int FM, int FN>
-__device__ __forceinline__ void store_blocks_counted(const void* Ctile, int64_t bytes, int64_t ldc, int64_t n_left,
-                                                     int lane, const f32x16 (&acc)[FM][FN]) {
+__device__ __forceinline__ void store16_vec(const void* Ctile, int64_t bytes, int64_t ldc, int64_t n_left, int lane,
+                                            const f32x4 (&acc)[FM][FN]) {
   const __amdgpu_buffer_rsrc_t rs = store_rsrc(Ctile, bytes);
-  const int li = lane & 31, lg = lane >> 5;
+  // an opaque copy of the lane index keeps the compiler from hoisting the
+  // row offsets and column masks out of the caller's loop (and spilling them)
+  uint32_t ln;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+  const uint32_t lr = ln & 15u, lc = 4u * (ln >> 4);
   constexpr uint32_t es = sizeof(Out);
-  const bool full = n_left >= FN * 32;
+  const bool full = n_left >= FN * 16;
+  const int32_t nl = n_left < FN * 16 ? (int32_t)n_left : FN * 16;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const uint32_t rowoff = (uint32_t)((i * 32 + li) * ldc) * es + 4u * lg * es;
+    const uint32_t rowoff = (16u * i + lr) * (uint32_t)ldc * es + lc * es;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t col = (uint32_t)(j * 32 + 8 * g);
-        const uint32_t off = (full || (int64_t)(col + 4 * lg) < n_left) ? rowoff + col * es : kOutOfRange;
-        const f32x16& a = acc[i][j];
-        if constexpr (es == 4) {
-          buf_store16(rs, off, __builtin_bit_cast(u32x4, f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]}));
-        } else {
-          buf_store8(rs, off, u32x2{pack2<Out>(a[4 * g], a[4 * g + 1]), pack2<Out>(a[4 * g + 2], a[4 * g + 3])});
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      const uint32_t col = (uint32_t)(16 * j);
+      const uint32_t off = (full || (int32_t)(col + lc) < nl) ? rowoff + col * es : kOutOfRange;
+      const f32x4& a = acc[i][j];
+      if constexpr (es == 4)
+        buf_store16(rs, off, __builtin_bit_cast(u32x4, a));
+      else
+        buf_store8(rs, off, u32x2{pack2<Out>(a[0], a[1]), pack2<Out>(a[2], a[3])});
+      __builtin_amdgcn_sched_barrier(0);
     }
+  }
+}
+
+// Element-wise store with bounds checks (any N, any alignment of ldc).
+template <typename Out, int FM, int FN>
+__device__ __forceinline__ void store16_elem(void* Cb, int64_t ldc, int64_t M, int64_t N, int64_t r0, int64_t c0,
+                                             int lane, const f32x4 (&acc)[FM][FN]) {
+  const int lr = lane & 15, lc = 4 * (lane >> 4);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t row = r0 + 16 * i + lr;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = c0 + 16 * j + lc + q;
+        if (row < M && col < N) store_out<Out>(Cb, row * ldc + col, acc[i][j][q]);
+      }
+  }
+}
+
+// acc = alpha * acc + beta * C + bias[col] in fp32 (C read only if beta != 0;
+// entries outside M x N are left alone and never stored).
+template <typename Out, int FM, int FN>
+__device__ __forceinline__ void epilogue16(const GemmArgs& args, const void* Cb, int64_t ldc, int64_t M, int64_t N,
+                                           int64_t r0, int64_t c0, int lane, f32x4 (&acc)[FM][FN]) {
+  const int lr = lane & 15, lc = 4 * (lane >> 4);
+  const float alpha = args.alpha, beta = args.beta;
+  const bool use_c = beta != 0.f, use_bias = args.bias != nullptr;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t row = r0 + 16 * i + lr;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = c0 + 16 * j + lc + q;
+        float v = alpha * acc[i][j][q];
+        if (row < M && col < N) {
+          if (use_c) v = __builtin_fmaf(beta, load_out<Out>(Cb, row * ldc + col), v);
+          if (use_bias) v += load_out<Out>(args.bias, col);
+        }
+        acc[i][j][q] = v;
+      }
   }
 }
 
 template <typename In, typename Out, bool TA, bool TB, bool EPI>
 __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(GemmArgs args) {
   constexpr int BM = 256, BN = 256, BK = 64, WN = 4;
-  constexpr int WTM = 128, WTN = 64, FM = WTM / 32, FN = WTN / 32, KS = BK / 16;
+  constexpr int WTM = 128, WTN = 64, FM = WTM / 16, FN = WTN / 16, KS = BK / 32;
   constexpr bool A_KC = !TA, B_KC = TB;
   using OA = DmaPair<A_KC, BM, BK, 4>;  // issued by the four waves of group 1
   using OB = DmaPair<B_KC, BN, BK, 4>;  // issued by the four waves of group 0
   constexpr uint32_t A_BYTES = OA::BYTES, B_BYTES = OB::BYTES;
   constexpr uint32_t B_BASE = 3 * A_BYTES;  // three A buffers, then two B buffers
   constexpr int PA = OA::IPW, PB = OB::IPW;  // copy instructions per wave per step
-  constexpr int ST = FM * FN * 4;            // store instructions of store_blocks_counted
+  constexpr int ST = FM * FN;                // store instructions of store16_vec
   static_assert(B_BASE + 2 * B_BYTES <= 160 * 1024, "LDS budget");
   static_assert(PA + ST < 64 && PB + ST < 64, "counted waits fit the vector-memory counter");
 
@@ -270,13 +353,13 @@ __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(GemmArgs args) {
   };
 
   // LDS byte offsets of this wave's fragment reads
-  FragAddr<A_KC, OA::CH, FM> fra;
-  FragAddr<B_KC, OB::CH, FN> frb;
+  FragAddr<A_KC, OA::CH> fra;
+  FragAddr<B_KC, OB::CH> frb;
   fra.init(wm0, lane);
   frb.init(wn0, lane);
-  constexpr uint32_t A_TR4 = 4 * OA::CH * 16, B_TR4 = 4 * OB::CH * 16;
+  constexpr uint32_t A_TR4 = decltype(fra)::TR4, B_TR4 = decltype(frb)::TR4;
 
-  f32x16 acc[FM][FN];
+  f32x4 acc[FM][FN];
   u32x4 fa[KS][FM], fb[KS][FN];
 
   // memory phase: this wave's fragments of every slice of the step held in
@@ -317,9 +400,9 @@ __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(GemmArgs args) {
         for (int jj = 0; jj < FN; ++jj) {
           const int j = (i & 1) ? FN - 1 - jj : jj;
           if (decltype(first)::value && ks == 0)
-            acc[i][j] = mfma32<In>(fb[ks][j], fa[ks][i], f32x16{});
+            acc[i][j] = mfma16<In>(fb[ks][j], fa[ks][i], f32x4{});
           else
-            acc[i][j] = mfma32<In>(fb[ks][j], fa[ks][i], acc[i][j]);
+            acc[i][j] = mfma16<In>(fb[ks][j], fa[ks][i], acc[i][j]);
         }
   };
   auto barrier = [&]() {
@@ -341,24 +424,21 @@ __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(GemmArgs args) {
     char* Cb = (char*)args.C + it.b * args.sC * (int64_t)sizeof(Out);
     const int64_t r0 = it.m0 + wm0, c0 = it.n0 + wn0;
     const bool in = r0 < M && c0 < N;
-    store_blocks_counted<Out, FM, FN>(in ? Cb + (r0 * ldc + c0) * (int64_t)sizeof(Out) : Cb,
-                                      in ? ((M - 1 - r0) * ldc + (N - c0)) * (int64_t)sizeof(Out) : 0, ldc,
-                                      in ? N - c0 : 0, lane, acc);
+    store16_vec<Out, FM, FN>(in ? Cb + (r0 * ldc + c0) * (int64_t)sizeof(Out) : Cb,
+                             in ? ((M - 1 - r0) * ldc + (N - c0)) * (int64_t)sizeof(Out) : 0, ldc, in ? N - c0 : 0,
+                             lane, acc);
   };
   auto store_final = [&](int64_t t) {
     const Item it = item_of(t);
     char* Cb = (char*)args.C + it.b * args.sC * (int64_t)sizeof(Out);
     const int64_t r0 = it.m0 + wm0, c0 = it.n0 + wn0;
     if (r0 >= M || c0 >= N) return;
-    if (N % 4 == 0 || it.n0 + BN <= N) {
-      char* Ct = Cb + (r0 * ldc + c0) * (int64_t)sizeof(Out);
-      const int64_t bytes = ((M - 1 - r0) * ldc + (N - c0)) * (int64_t)sizeof(Out);
-      if constexpr (EPI) epilogue_acc_vec<Out, FM, FN>(args, Ct, bytes, ldc, N - c0, c0, lane, acc);
-      store_tile_vec<Out, FM, FN>(Ct, bytes, ldc, N - c0, lane, acc);
-    } else {
-      if constexpr (EPI) epilogue_acc<Out, FM, FN>(args, Cb, ldc, M, N, r0, c0, lane, acc);
-      store_tile<Out, FM, FN>(Cb, ldc, M, N, r0, c0, lane, acc);
-    }
+    if constexpr (EPI) epilogue16<Out, FM, FN>(args, Cb, ldc, M, N, r0, c0, lane, acc);
+    if (N % 4 == 0 || it.n0 + BN <= N)
+      store16_vec<Out, FM, FN>(Cb + (r0 * ldc + c0) * (int64_t)sizeof(Out),
+                               ((M - 1 - r0) * ldc + (N - c0)) * (int64_t)sizeof(Out), ldc, N - c0, lane, acc);
+    else
+      store16_elem<Out, FM, FN>(Cb, ldc, M, N, r0, c0, lane, acc);
   };
 
   // Copy schedule (global step g; A in buffer g mod 3, B in buffer g mod 2):
