@@ -71,6 +71,17 @@ typedef enum {
 #define TG_TILE_PINGPONG 23
 #define TG_TILE_PINGPONG_EPI 24
 
+/* Entry of the TG_VARIANT_TILE table served by the panel kernel, for products
+ * with a short K whose time goes into writing C ("Triton Optimization
+ * Reference", section 7: persistent programs looping over tiles).  Each
+ * work-group walks a run of 128 x 128 tiles along one row panel of C, with A's
+ * 128 x K panel held in registers and B's tiles in two LDS buffers, so
+ * lds_bytes = 2 * bk * bn * 2 with bk = 128, the largest K it takes.  It
+ * serves A stored M x K, 0 < K <= 128, N a multiple of 16 bytes' worth of
+ * output elements, and no epilogue.  The run calls send any other call
+ * planned on this entry to the 128 x 128 tile kernel (entry 13). */
+#define TG_TILE_PANEL 25
+
 /* plan.flags bits */
 #define TG_FLAG_EVEN_K 0x1 /* K is a multiple of the K-tile: no masked K step */
 #define TG_FLAG_VEC16 0x2  /* leading dims and contiguous extents allow 16-byte loads */

@@ -25,6 +25,7 @@ TG_BF16, TG_FP16, TG_FP32 = 0, 1, 2
 TG_OK, TG_ERR_INVALID, TG_ERR_UNSUPPORTED, TG_ERR_HIP = 0, 1, 2, 3
 VARIANT_GENERIC, VARIANT_TILE, VARIANT_SKINNY = 0, 1, 2
 TILE_PINGPONG, TILE_PINGPONG_EPI = 23, 24  # TG_TILE_PINGPONG, TG_TILE_PINGPONG_EPI
+TILE_PANEL = 25  # TG_TILE_PANEL
 FLAG_EVEN_K, FLAG_VEC16, FLAG_ROTATE_K, FLAG_PERSIST, FLAG_PREFETCH, FLAG_STREAM_C = 0x1, 0x2, 0x4, 0x8, 0x10, 0x20
 
 

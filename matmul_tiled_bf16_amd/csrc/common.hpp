@@ -34,6 +34,7 @@ struct GemmArgs {
   float alpha, beta;
   const void* bias;
   int32_t stream_c;  // nonzero: LDS-staged C stores are non-temporal
+  int32_t span;      // panel kernel: column tiles per run of a work-group
 };
 
 using KernelFn = void (*)(GemmArgs);

@@ -9,6 +9,7 @@
 #include "tiles.hpp"
 #include "tile_gemm.hpp"
 #include "pingpong_gemm.hpp"
+#include "panel_gemm.hpp"
 #include "generic_gemm.hpp"
 
 
@@ -22,6 +23,10 @@ constexpr KernelFn tile_k() {
     return &pingpong_gemm_kernel<TG_IN, TG_OUT, TG_TA != 0, TG_TB != 0, false>;
   else if constexpr (s.kind == kPingPongEpi)
     return &pingpong_gemm_kernel<TG_IN, TG_OUT, TG_TA != 0, TG_TB != 0, true>;
+  else if constexpr (s.kind == kPanel && TG_TA == 0)
+    return &panel_gemm_kernel<TG_IN, TG_OUT, TG_TB != 0>;
+  else if constexpr (s.kind == kPanel)
+    return nullptr;  // A stored K x M: the launcher sends these to a tile kernel
   else
     return &tile_gemm_kernel<TG_IN, TG_OUT, s.bm, s.bn, s.bk, s.wm, s.wn, s.stages, s.occ,
                              s.dw ? s.dw : s.wm * s.wn, TG_TA != 0, TG_TB != 0>;

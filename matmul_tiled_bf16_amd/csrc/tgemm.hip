@@ -87,6 +87,14 @@ bool skinny_ok(const gemm_plan_t& p) {
          p.k >= 8 && 2 * (64 * p.ldb + p.k) < lim && 2 * (32 * p.lda + p.k) < lim;
 }
 
+// The panel kernel (short K, A resident in registers along a row panel):
+// A stored M x K, 0 < K <= 128, and N a whole number of 16-byte output units
+// for its LDS-staged row-segment stores; on top of vec_ok.
+bool panel_ok(const gemm_plan_t& p) {
+  const int64_t units = p.out_type == TG_FP32 ? 4 : 8;
+  return !p.trans_a && p.k > 0 && p.k <= tg::kPanelKMax && p.n % units == 0;
+}
+
 bool skinny_fits(int t, int64_t m) { return m <= 16 * kSkinny[t].mb; }
 
 int skinny_choose(int64_t m, int64_t) { return m > 16 ? 1 : 0; }
@@ -97,17 +105,24 @@ int skinny_choose(int64_t m, int64_t) { return m > 16 ? 1 : 0; }
 //  * MFMA-bound problems (arithmetic intensity above MI355X's ~312 FLOP/B
 //    ridge) take the 256x256 ping-pong kernel (8 waves alternating MFMA and
 //    memory phases) when there are >= 2 items per CU;
-//  * HBM-bound ones take 128x128 tiles, two work-groups per CU, whose
+//  * HBM-bound ones with K <= 128 and >= 2048 tiles take the panel kernel
+//    (runs of 128x128 tiles along a row panel of C: the next tile's B copy
+//    overlaps this tile's stores);
+//  * other HBM-bound ones take 128x128 tiles, two work-groups per CU, whose
 //    operand panels and 1 KiB row-segment stores keep the streams long;
 //  * small and ragged problems take smaller tiles so that there are at least
 //    ~256 work-groups.
-int choose_tile(int64_t m, int64_t n, int64_t k, int64_t batch, int out_size) {
+int choose_tile(const gemm_plan_t& p, int64_t batch) {
+  const int64_t m = p.m, n = p.n, k = p.k;
+  const int out_size = p.out_type == TG_FP32 ? 4 : 2;
   auto items = [&](int t) { return cdiv(m, kTiles[t].bm) * cdiv(n, kTiles[t].bn) * batch; };
   if (m <= 32) return 5;
   const double flops = 2.0 * (double)m * (double)n * (double)k;
   const double bytes = 2.0 * ((double)m * k + (double)k * n) + (double)out_size * m * n;
   const bool mfma_bound = bytes > 0 && flops / bytes > 312.5;
   if (mfma_bound && items(8) >= 512 && k > 0) return tg::kPingPongTile;  // 256x256, 8 waves
+  // short K and many tiles: runs along row panels, A held in registers
+  if (!mfma_bound && panel_ok(p) && items(tg::kPanelTile) >= 2048) return tg::kPanelTile;
   if (items(13) >= 256) return mfma_bound ? 1 : 13;  // 128x128
   return 0;                                          // 64x64
 }
@@ -228,7 +243,7 @@ tg_status bmm_plan(gemm_plan_t* plan, tg_dtype in_type, tg_dtype out_type, int t
     p.tile = skinny_choose(m, n);
   } else if (p.flags & TG_FLAG_VEC16) {
     p.variant = TG_VARIANT_TILE;
-    p.tile = choose_tile(m, n, k, batch, out_type == TG_FP32 ? 4 : 2);
+    p.tile = choose_tile(p, batch);
   } else {
     p.variant = TG_VARIANT_GENERIC;
     p.tile = choose_generic(m, n, batch);
@@ -346,7 +361,8 @@ static tg_status launch(const gemm_plan_t* plan, const gemm_epilogue_t* epi, int
   // The ping-pong kernel: its epilogue entry when there is an epilogue; the
   // 8-wave tile kernel for K = 0 (which it does not handle) and for more
   // items than its 32-bit item order covers.
-  const bool pingpong = variant == TG_VARIANT_TILE && kTiles[tile].kind != tg::kTileKernel;
+  const bool pingpong = variant == TG_VARIANT_TILE &&
+                        (kTiles[tile].kind == tg::kPingPong || kTiles[tile].kind == tg::kPingPongEpi);
   if (pingpong) {
     const int64_t items = cdiv(p.m, kTiles[tile].bm) * cdiv(p.n, kTiles[tile].bn) * batch;
     if (p.k == 0 || items >= ((int64_t)1 << 30))
@@ -354,6 +370,9 @@ static tg_status launch(const gemm_plan_t* plan, const gemm_epilogue_t* epi, int
     else
       tile = a.epi ? tg::kPingPongEpiTile : tg::kPingPongTile;
   }
+  // The panel kernel; what it does not serve goes to the 128 x 128 tile.
+  if (variant == TG_VARIANT_TILE && kTiles[tile].kind == tg::kPanel && (a.epi || !panel_ok(p))) tile = 13;
+  a.span = 0;
   const Launch l = launch_shape(variant, tile);
   const int io = p.in_type == TG_BF16 ? 0 : 1, oo = p.out_type == TG_FP32 ? 0 : 1;
   KernelFn fn;
@@ -376,9 +395,17 @@ static tg_status launch(const gemm_plan_t* plan, const gemm_epilogue_t* epi, int
     // one work-group per (matrix, tile) work item, flattened; beyond 2^30
     // items each work-group loops (the stride stays a multiple of 8, which
     // keeps every item on the XCD the kernel's tile order assumes)
-    const int64_t total = groups * batch;
+    int64_t total = groups * batch;
     int64_t cap = (int64_t)1 << 30;
-    if (variant == TG_VARIANT_TILE && kTiles[tile].kind == tg::kPingPong) {
+    if (variant == TG_VARIANT_TILE && kTiles[tile].kind == tg::kPanel) {
+      // one work-group per run of column tiles: whole row panels, halved
+      // while there are fewer than 4 runs per CU (down to 4 tiles a run)
+      const int64_t target = 4 * (int64_t)compute_units();
+      int32_t span = a.tiles_n;
+      while (span > 4 && batch * a.tiles_m * cdiv(a.tiles_n, span) < target) span = (span + 1) / 2;
+      a.span = span;
+      total = batch * a.tiles_m * cdiv(a.tiles_n, span);
+    } else if (variant == TG_VARIANT_TILE && kTiles[tile].kind == tg::kPingPong) {
       // persistent ping-pong: one work-group per CU; it stores each finished
       // tile with 4-column vector stores (N % 4 == 0) and has no epilogue
       const int64_t slots = (int64_t)compute_units();

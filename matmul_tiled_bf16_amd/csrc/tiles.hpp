@@ -13,7 +13,8 @@ namespace tg {
 enum TileKind {
   kTileKernel = 0,  // tile_gemm_kernel (tile_gemm.hpp)
   kPingPong = 1,    // pingpong_gemm_kernel without epilogue: persistent when there is enough work
-  kPingPongEpi = 2  // pingpong_gemm_kernel with the alpha/beta/bias epilogue (one tile per work-group)
+  kPingPongEpi = 2,  // pingpong_gemm_kernel with the alpha/beta/bias epilogue (one tile per work-group)
+  kPanel = 3         // panel_gemm_kernel: short K, A resident in registers along a row panel of C
 };
 
 struct TileShape {
@@ -60,8 +61,13 @@ constexpr TileShape kTiles[] = {
     // B LDS buffers (160 KiB); the second entry adds the epilogue
     {256, 256, 64, 2, 4, 2, 1, 4, kPingPong},     // 23
     {256, 256, 64, 2, 4, 2, 1, 4, kPingPongEpi},  // 24
+    // 4 waves walking runs of 128 x 128 tiles along a row panel of C, K <=
+    // 128 (panel_gemm.hpp): A in registers, two B LDS buffers (64 KiB), two
+    // work-groups per CU
+    {128, 128, 128, 2, 2, 2, 2, 0, kPanel},  // 25
 };
-constexpr int kPingPongTile = 23, kPingPongEpiTile = 24;
+constexpr int kPingPongTile = 23, kPingPongEpiTile = 24, kPanelTile = 25;
+constexpr int kPanelKMax = kTiles[kPanelTile].bk;  // the panel kernel holds all of K at once
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 // Tiles a grouped launch may take (indices into kTiles): small and ragged
@@ -78,7 +84,9 @@ constexpr TileShape kGenericTiles[] = {
 constexpr int kNumGeneric = sizeof(kGenericTiles) / sizeof(kGenericTiles[0]);
 
 constexpr int lds_bytes_of(const TileShape& t) {
-  return t.kind != kTileKernel ? (3 * t.bm * t.bk + 2 * t.bk * t.bn) * 2 : t.stages * (t.bm * t.bk + t.bk * t.bn) * 2;
+  return t.kind == kPanel ? t.stages * t.bk * t.bn * 2
+         : t.kind != kTileKernel ? (3 * t.bm * t.bk + 2 * t.bk * t.bn) * 2
+                                 : t.stages * (t.bm * t.bk + t.bk * t.bn) * 2;
 }
 
 // Whether the tile kernel can run persistently: the first wait of a

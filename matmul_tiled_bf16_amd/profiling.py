@@ -32,7 +32,8 @@ COPY_BYTES = 1 << 30  # bytes read and written by one calibration copy
 
 # kernel families: the kernels' name patterns and the sources they are built from
 FAMILIES = {
-    "gemm": (("tile_gemm_kernel", "pingpong_gemm_kernel", "skinny_gemm_kernel", "generic_gemm_kernel"),
+    "gemm": (("tile_gemm_kernel", "pingpong_gemm_kernel", "panel_gemm_kernel", "skinny_gemm_kernel",
+              "generic_gemm_kernel"),
              lambda f: not os.path.basename(f).startswith("attention")),
     "group": (("group_gemm_kernel",), lambda f: not os.path.basename(f).startswith("attention")),
     "attention": (("attn_fwd_kernel",),

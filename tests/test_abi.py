@@ -171,6 +171,14 @@ def test_plan_choices_for_the_workloads():
         assert p.flags & tg.FLAG_STREAM_C  # outputs of 128 MiB and 2 GiB: non-temporal stores
         assert tg.plan_tile(p, tg.VARIANT_TILE, 1).flags & tg.FLAG_STREAM_C  # kept by a re-plan
     assert not tg.plan(2048, 2048, 128, trans_b=True).flags & tg.FLAG_STREAM_C  # 16 MiB: stays cached
+    # short K with many tiles: the panel kernel (A stored M x K); A stored K x M, a long K, or too few
+    # tiles keep the 128 x 128 tile kernel
+    assert tg.plan(2048, 2048, 128, trans_b=True, batch=128).tile == tg.TILE_PANEL
+    assert tg.plan(2048, 2048, 64, batch=128, out_dtype=torch.bfloat16).tile == tg.TILE_PANEL
+    assert tg.plan(2048, 2048, 128, trans_a=True, trans_b=True, batch=128).tile == 13
+    assert tg.plan(2048, 2048, 136, trans_b=True, batch=128).tile == 13
+    assert tg.plan(2048, 2048, 128, trans_b=True).tile == 13
+    assert tg.plan(2048, 128, 2048, batch=128).tile == 13
     with pytest.raises(tg.TgError):
         tg.plan(64, 64, 64, batch=0)
     p = tg.plan(8192, 8192, 8192, out_dtype=torch.bfloat16)
@@ -187,12 +195,16 @@ def test_odd_shapes_take_the_generic_loader():
 
 
 def test_lds_budget_matches_the_staging_formula_and_fits():
-    for m, n, k in [(256, 256, 256), (1000, 1000, 1000), (8192, 8192, 8192), (2048, 128, 2048), (17, 33, 63)]:
+    for m, n, k in [(256, 256, 256), (1000, 1000, 1000), (8192, 8192, 8192), (2048, 128, 2048), (17, 33, 63),
+                    (2048, 2048, 128)]:
         st, p = raw_plan(m=m, n=n, k=k)
         assert st == tg.TG_OK
         if p.variant == tg.VARIANT_TILE and p.tile in (tg.TILE_PINGPONG, tg.TILE_PINGPONG_EPI):
             # three A and two B buffers of one K step
             assert p.lds_bytes == (3 * p.bm * p.bk + 2 * p.bk * p.bn) * 2
+        elif p.variant == tg.VARIANT_TILE and p.tile == tg.TILE_PANEL:
+            # two B buffers holding all of K
+            assert p.lds_bytes == 2 * p.bk * p.bn * 2
         elif p.variant != tg.VARIANT_SKINNY:
             assert p.lds_bytes == roofline.lds_budget(p.bm, p.bn, p.bk, p.stages)
         assert p.lds_bytes <= roofline.MI355X_LDS_PER_WORKGROUP
@@ -330,5 +342,6 @@ def test_python_constants_match_the_header():
     defs = dict(re.findall(r"#define\s+(TG_\w+)\s+(0x[0-9a-fA-F]+|\d+)", text))
     assert int(defs["TG_TILE_PINGPONG"], 0) == tg.TILE_PINGPONG
     assert int(defs["TG_TILE_PINGPONG_EPI"], 0) == tg.TILE_PINGPONG_EPI
+    assert int(defs["TG_TILE_PANEL"], 0) == tg.TILE_PANEL
     for name in ("EVEN_K", "VEC16", "ROTATE_K", "PERSIST", "PREFETCH", "STREAM_C"):
         assert int(defs["TG_FLAG_" + name], 0) == getattr(tg, "FLAG_" + name)
