@@ -35,6 +35,7 @@ struct GemmArgs {
   const void* bias;
   int32_t stream_c;  // nonzero: LDS-staged C stores are non-temporal
   int32_t span;      // panel kernel: column tiles per run of a work-group
+  int32_t nt_ab;     // tile kernel: bit 0 (1): A, bit 1 (2): B is read by one tile only -- non-temporal loads
 };
 
 using KernelFn = void (*)(GemmArgs);

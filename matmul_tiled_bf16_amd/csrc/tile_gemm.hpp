@@ -57,11 +57,26 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
 // the resource's size read as zero.  Issued as inline assembly so that the
 // compiler neither waits on it before unrelated LDS reads nor reorders it
 // across the explicit waits below: the kernel counts these loads itself.
+// With `nt` the load carries the non-temporal hint: for operand bytes that
+// no other tile of the launch reads, so that streaming them through the L2
+// does not evict the lines other tiles still share.
 __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(rsrc), "s"(lds_addr)
                : "m0");
+}
+__device__ __forceinline__ void dma16_nt(const i32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_addr)
+               : "m0");
+}
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t lds_addr, bool nt) {
+  if (nt)
+    dma16_nt(rsrc, voff, lds_addr);
+  else
+    dma16(rsrc, voff, lds_addr);
 }
 
 // s_waitcnt vmcnt(N), optionally with lgkmcnt(0) (gfx9 encoding: vmcnt[3:0]
@@ -146,23 +161,24 @@ struct DmaOperand {
 
   // Instruction i of this wave's share (0 <= i < IPW).
   template <bool MASK_K>
-  __device__ __forceinline__ void issue_one(int i, const i32x4& rs, uint32_t tile_lds, int wave, int64_t k_left) const {
+  __device__ __forceinline__ void issue_one(int i, const i32x4& rs, uint32_t tile_lds, int wave, int64_t k_left,
+                                            bool nt = false) const {
     uint32_t off = voff[i];
     if constexpr (MASK_K && KC) off = (int64_t)kofs[i] < k_left ? off : kOutOfRange;
-    dma16(rs, off, tile_lds + (uint32_t)(wave * IPW + i) * 1024u);
+    dma16(rs, off, tile_lds + (uint32_t)(wave * IPW + i) * 1024u, nt);
   }
 
   // base: element (mn0, k0) [KC] or (k0, mn0) [MN]; bytes: from base to the
   // end of the matrix's last element; k_left = K - k0.
   template <bool MASK_K>
   __device__ __forceinline__ void issue(const uint16_t* base, int64_t bytes, uint32_t tile_lds, int wave,
-                                        int64_t k_left) const {
+                                        int64_t k_left, bool nt = false) const {
     const i32x4 rs = make_rsrc(base, bytes);
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       uint32_t off = voff[i];
       if constexpr (MASK_K && KC) off = (int64_t)kofs[i] < k_left ? off : kOutOfRange;
-      dma16(rs, off, tile_lds + (uint32_t)(wave * IPW + i) * 1024u);
+      dma16(rs, off, tile_lds + (uint32_t)(wave * IPW + i) * 1024u, nt);
     }
   }
 };
@@ -608,6 +624,8 @@ __device__ __forceinline__ void tile_gemm_body(const KA& kargs) {
     ld_step = 0;
     seek();
   };
+  // operands no other tile of the launch reads are loaded non-temporally
+  const bool nt_a = !GROUP && (args.nt_ab & 1), nt_b = !GROUP && (args.nt_ab & 2);
   bool prefetched = false;  // this item's prologue copies were issued by the previous item
   bool behind_stores = false;  // ... and this wave's stores of that item were issued after them
 
@@ -618,11 +636,11 @@ __device__ __forceinline__ void tile_gemm_body(const KA& kargs) {
       const uint32_t st = lds0 + buf * STAGE;
       if (!copier) {
       } else if (decltype(full)::value || k_left >= BK) {
-        oa.template issue<false>((const uint16_t*)a_ptr, a_left, st, dwave, k_left);
-        ob.template issue<false>((const uint16_t*)b_ptr, b_left, st + A_BYTES, dwave, k_left);
+        oa.template issue<false>((const uint16_t*)a_ptr, a_left, st, dwave, k_left, nt_a);
+        ob.template issue<false>((const uint16_t*)b_ptr, b_left, st + A_BYTES, dwave, k_left, nt_b);
       } else {
-        oa.template issue<true>((const uint16_t*)a_ptr, a_left, st, dwave, k_left);
-        ob.template issue<true>((const uint16_t*)b_ptr, b_left, st + A_BYTES, dwave, k_left);
+        oa.template issue<true>((const uint16_t*)a_ptr, a_left, st, dwave, k_left, nt_a);
+        ob.template issue<true>((const uint16_t*)b_ptr, b_left, st + A_BYTES, dwave, k_left, nt_b);
       }
       ++ld_step;
       seek();
@@ -676,9 +694,9 @@ __device__ __forceinline__ void tile_gemm_body(const KA& kargs) {
     auto dma_one = [&](int d, const i32x4& ra, const i32x4& rb, uint32_t dst) {
       if (!copier) return;
       if (d < OA::IPW)
-        oa.template issue_one<false>(d, ra, dst, dwave, BK);
+        oa.template issue_one<false>(d, ra, dst, dwave, BK, nt_a);
       else
-        ob.template issue_one<false>(d - OA::IPW, rb, dst + A_BYTES, dwave, BK);
+        ob.template issue_one<false>(d - OA::IPW, rb, dst + A_BYTES, dwave, BK, nt_b);
     };
     auto slice = [&](const Frags<FM, FN>& cur, Frags<FM, FN>* nxt, uint32_t nbase, int nks, const i32x4* rsa,
                      const i32x4* rsb, uint32_t dma_st, int d0, int cnt) {
