@@ -110,8 +110,8 @@ int skinny_choose(int64_t m, int64_t) { return m > 16 ? 1 : 0; }
 //    overlaps this tile's stores);
 //  * other HBM-bound ones take 128x128 tiles, two work-groups per CU, whose
 //    operand panels and 1 KiB row-segment stores keep the streams long;
-//  * small and ragged problems take smaller tiles so that there are at least
-//    ~256 work-groups.
+//  * small and ragged problems take 64x64 tiles so that there are at least
+//    ~256 work-groups, with a 4-deep ring when K is long.
 int choose_tile(const gemm_plan_t& p, int64_t batch) {
   const int64_t m = p.m, n = p.n, k = p.k;
   const int out_size = p.out_type == TG_FP32 ? 4 : 2;
@@ -124,7 +124,10 @@ int choose_tile(const gemm_plan_t& p, int64_t batch) {
   // short K and many tiles: runs along row panels, A held in registers
   if (!mfma_bound && panel_ok(p) && items(tg::kPanelTile) >= 2048) return tg::kPanelTile;
   if (items(13) >= 256) return mfma_bound ? 1 : 13;  // 128x128
-  return 0;                                          // 64x64
+  // 64x64: with a long K the 4-deep ring keeps three steps' copies in flight
+  // (1000^3: 12.3 -> 11.1 us); with a short one the 2-deep ring's shorter
+  // prologue wins (256^3: 5.5 vs 5.9 us)
+  return k >= 512 ? 26 : 0;
 }
 
 int choose_generic(int64_t m, int64_t n, int64_t batch) { return cdiv(m, 128) * cdiv(n, 128) * batch >= 256 ? 1 : 0; }

@@ -65,6 +65,11 @@ constexpr TileShape kTiles[] = {
     // 128 (panel_gemm.hpp): A in registers, two B LDS buffers (64 KiB), two
     // work-groups per CU
     {128, 128, 128, 2, 2, 2, 2, 0, kPanel},  // 25
+    // 64x64 tiles with deep rings for small, latency-bound products: with
+    // a K step's MFMAs far shorter than a copy's round trip, the time per
+    // step is the round trip divided by the steps in flight
+    {64, 64, 64, 2, 2, 4, 2},  // 26: 4-deep ring, 64 KiB
+    {64, 64, 32, 2, 2, 5, 3},  // 27: 5-deep ring of 32-deep steps, 40 KiB
 };
 constexpr int kPingPongTile = 23, kPingPongEpiTile = 24, kPanelTile = 25;
 constexpr int kPanelKMax = kTiles[kPanelTile].bk;  // the panel kernel holds all of K at once

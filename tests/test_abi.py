@@ -146,11 +146,13 @@ def test_plan_choices_for_the_workloads():
     p = tg.plan(256, 256, 256)
     assert (p.variant, p.bm, p.bn, p.flags & tg.FLAG_EVEN_K, p.flags & tg.FLAG_VEC16) == (
         tg.VARIANT_TILE, 64, 64, tg.FLAG_EVEN_K, tg.FLAG_VEC16)
+    assert (p.tile, p.stages) == (0, 2)  # short K: the 2-deep ring
     # 1000^3, every transpose: vector path (1000 = 8*125), ragged K tail
     for ta in (0, 1):
         for tb in (0, 1):
             p = tg.plan(1000, 1000, 1000, trans_a=ta, trans_b=tb)
             assert p.variant == tg.VARIANT_TILE and p.flags & tg.FLAG_VEC16 and not p.flags & tg.FLAG_EVEN_K
+            assert (p.tile, p.bm, p.bn, p.stages) == (26, 64, 64, 4)  # small, long K: the 4-deep 64x64 ring
             assert p.tiles_m * p.tiles_n >= 64
     # skinny M = 16, B stored N x K
     import torch
