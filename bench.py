@@ -17,6 +17,8 @@ Workloads (seeded synthetic inputs from synth/):
                 fp32 out (the same two products fused; MFMA-bound)
   group_moe     32 ragged expert GEMMs (8192 tokens, K = N = 1024, NN, bf16 out)
                 in one grouped launch; also times one launch per problem
+  splitk_long   1024 x 1024 x 65536 NN, bf16 out, K split into parts (gemm_splitk_run);
+                also times the same product as one plain launch
   ragged_1000   1000^3 NN, fp32 out
   square_256    256^3 NN, fp32 out
 
@@ -107,6 +109,8 @@ def main():
         return run_attention(args, torch, tg, profiling)
     if args.workload == "group_moe":
         return run_group(args, torch, tg, profiling)
+    if args.workload == "splitk_long":
+        return run_splitk(args, torch, tg, profiling)
 
     (p,) = problems(args.workload)
     dev = torch.device("cuda:0")
@@ -404,6 +408,85 @@ def run_group(args, torch, tg, profiling):
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_group(p, "TFLOP/s", args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def run_splitk(args, torch, tg, profiling):
+    """Split-K: one step = one gemm_splitk_run (a grouped launch of the K parts
+    into an fp32 workspace, then the reduction) at the suggested split count.
+    The product is MFMA-bound (arithmetic intensity above the ridge), but its
+    64 output tiles leave most of the 256 CUs idle as one plain launch, which
+    is timed the same way for comparison.  The roofline's duration is the
+    step's (both kernels)."""
+    import synth
+    (p,) = synth.long_k()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    A, B = up(p.A), up(p.B)
+    Cs = [torch.empty((p.m, p.n), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    pl = tg.plan(p.m, p.n, p.k, in_dtype=torch.bfloat16, out_dtype=torch.bfloat16)
+    splits = tg.splitk_choose(pl)
+    need = tg.splitk_workspace_bytes(pl, splits)
+    ws = torch.empty((need + 3) // 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        tg.gemm_splitk_run(pl, splits, ws, need, A, B, Cs[i % 2], stream)
+
+    def step_plain(i):
+        tg.gemm_run(pl, A, B, Cs[i % 2], stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    assert torch.isfinite(Cs[0].float()).all().item(), "non-finite output"
+    mean_ms, kms, queued_ahead = gated_kernel_ms(torch, stream, step, args.steps, max(args.warmup, 1))
+    plain_ms, _, plain_ahead = gated_kernel_ms(torch, stream, step_plain, max(args.steps // 2, 3), 2)
+    flops = p.flops
+    nbytes = 2 * (p.m * p.k + p.k * p.n) + 2 * p.m * p.n
+    kernel_s = mean_ms / 1e3
+    achieved = flops / kernel_s / 1e12
+    tflops = flops / (ms_per_step / 1e3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": p.name, "m": p.m, "n": p.n, "k": p.k, "op": "NN", "in_dtype": "bf16",
+                   "out_dtype": "bf16", "splits": splits, "workspace_bytes": need},
+        "tflops": round(tflops, 2),
+        "pct_mfma_peak": round(100 * flops / (ms_per_step / 1e3) / PEAK_MFMA, 2),
+        "gbps": round(nbytes / (ms_per_step / 1e3) / 1e9, 1),
+        "pct_hbm_peak": round(100 * nbytes / (ms_per_step / 1e3) / PEAK_HBM, 2),
+        "plain_launch": {"kernel_ms": round(plain_ms, 5), "tile_index": int(pl.tile),
+                         "queued_ahead": bool(plain_ahead), "splitk_speedup": round(plain_ms / mean_ms, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA / 1e12, "unit": "TFLOP/s",
+                     "frac": round(achieved * 1e12 / PEAK_MFMA, 4), "traffic": None,
+                     "kernel_ms": round(kernel_s * 1e3, 5),
+                     "kernel_ms_each_min": round(float(np.min(kms)), 5),
+                     "kernel_ms_each_p90": round(float(np.percentile(kms, 90)), 5),
+                     "launches_queued_ahead": bool(queued_ahead),
+                     "algorithmic": {"flops": flops, "bytes": nbytes}},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(p, "TFLOP/s", args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

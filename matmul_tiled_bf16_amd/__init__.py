@@ -26,6 +26,7 @@ TG_OK, TG_ERR_INVALID, TG_ERR_UNSUPPORTED, TG_ERR_HIP = 0, 1, 2, 3
 VARIANT_GENERIC, VARIANT_TILE, VARIANT_SKINNY = 0, 1, 2
 TILE_PINGPONG, TILE_PINGPONG_EPI = 23, 24  # TG_TILE_PINGPONG, TG_TILE_PINGPONG_EPI
 TILE_PANEL = 25  # TG_TILE_PANEL
+SPLITK_MAX = 32  # TG_SPLITK_MAX
 FLAG_EVEN_K, FLAG_VEC16, FLAG_ROTATE_K, FLAG_PERSIST, FLAG_PREFETCH, FLAG_STREAM_C = 0x1, 0x2, 0x4, 0x8, 0x10, 0x20
 
 
@@ -111,6 +112,12 @@ def lib() -> ctypes.CDLL:
                                      ctypes.POINTER(GroupProblem), i64, i32, p]
         L.tg_group_tiles.restype = i32
         L.tg_group_tiles.argtypes = []
+        L.gemm_splitk_run.restype = ctypes.c_int
+        L.gemm_splitk_run.argtypes = [ctypes.POINTER(GemmPlan), i32, p, ctypes.c_uint64, p, p, p, p]
+        L.tg_splitk_workspace_bytes.restype = ctypes.c_uint64
+        L.tg_splitk_workspace_bytes.argtypes = [ctypes.POINTER(GemmPlan), i32]
+        L.tg_splitk_choose.restype = i32
+        L.tg_splitk_choose.argtypes = [ctypes.POINTER(GemmPlan)]
         L.attention_fwd.restype = ctypes.c_int
         L.attention_fwd.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
                                     p, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, p]
@@ -174,7 +181,9 @@ def _stream_handle(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _ptr(t) -> int:
+def _ptr(t):
+    if t is None:
+        return None  # a null pointer
     return t.data_ptr() if hasattr(t, "data_ptr") else int(t)
 
 
@@ -253,6 +262,53 @@ def gemm(A, B, *, trans_a: bool = False, trans_b: bool = False, out_dtype=None, 
     p = plan(m, n, k, trans_a=trans_a, trans_b=trans_b, in_dtype=A.dtype, out_dtype=out_dtype, lda=_ld(A),
              ldb=_ld(B), ldc=_ld(out))
     gemm_run_ex(p, A, B, out, alpha=alpha, beta=beta, bias=bias, stream=stream)
+    return out
+
+
+def splitk_workspace_bytes(p: GemmPlan, splits: int) -> int:
+    """tg_splitk_workspace_bytes(): bytes of fp32 workspace gemm_splitk_run needs."""
+    return int(lib().tg_splitk_workspace_bytes(ctypes.byref(p), int(splits)))
+
+
+def splitk_choose(p: GemmPlan) -> int:
+    """tg_splitk_choose(): a split count for the plan's product (1: do not split)."""
+    return int(lib().tg_splitk_choose(ctypes.byref(p)))
+
+
+def gemm_splitk_run(p: GemmPlan, splits: int, workspace, workspace_bytes: int, A, B, C, stream=None) -> None:
+    """gemm_splitk_run(): raw call (pointers or tensors)."""
+    st = lib().gemm_splitk_run(ctypes.byref(p), int(splits), _ptr(workspace), int(workspace_bytes), _ptr(A), _ptr(B),
+                               _ptr(C), _stream_handle(stream))
+    if st != TG_OK:
+        raise TgError(st, "gemm_splitk_run")
+
+
+def gemm_splitk(A, B, *, trans_a: bool = False, trans_b: bool = False, out_dtype=None, out=None,
+                splits: Optional[int] = None, workspace=None, stream=None):
+    """C = op(A) @ op(B) with K split into parts (gemm_splitk_run); splits defaults to
+    tg_splitk_choose's suggestion.  The fp32 workspace is a caller tensor (allocated here
+    when not given).  Returns C."""
+    import torch
+    _check_matrix(A, "A")
+    _check_matrix(B, "B")
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must have the same dtype")
+    m, k = (A.shape[1], A.shape[0]) if trans_a else (A.shape[0], A.shape[1])
+    kb, n = (B.shape[1], B.shape[0]) if trans_b else (B.shape[0], B.shape[1])
+    if kb != k:
+        raise ValueError(f"inner dimensions differ: {k} vs {kb}")
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=A.device)
+    elif out.shape != (m, n) or out.dtype != out_dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    p = plan(m, n, k, trans_a=trans_a, trans_b=trans_b, in_dtype=A.dtype, out_dtype=out_dtype, lda=_ld(A),
+             ldb=_ld(B), ldc=_ld(out))
+    splits = splitk_choose(p) if splits is None else int(splits)
+    need = splitk_workspace_bytes(p, splits)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16) + 3) // 4, dtype=torch.float32, device=A.device)
+    gemm_splitk_run(p, splits, workspace, workspace.numel() * workspace.element_size(), A, B, out, stream)
     return out
 
 

@@ -36,7 +36,8 @@ IO = [("bf16", "f32"), ("bf16", "bf16"), ("f16", "f32"), ("f16", "f16")]
 def _units():
     units = [("tgemm", os.path.join(CSRC, "tgemm.hip"), []),
              ("inst_skinny", os.path.join(CSRC, "inst_skinny.hip"), []),
-             ("attention", os.path.join(CSRC, "attention.hip"), [])]
+             ("attention", os.path.join(CSRC, "attention.hip"), []),
+             ("splitk", os.path.join(CSRC, "splitk.hip"), [])]
     for i, o in IO:
         for ta in (0, 1):
             for tb in (0, 1):

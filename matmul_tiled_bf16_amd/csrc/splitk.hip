@@ -1,0 +1,146 @@
+// splitk.hip -- split-K products: C = op(A) op(B) with K cut into parts that
+// run as independent products, for shapes with too few output tiles to fill
+// the chip and a long K ("Triton Optimization Reference", section 7: the
+// persistent / stream-K family of schedules for when the tile grid alone
+// leaves compute units idle).
+//
+// The parts go out as one grouped launch (gemm_group_run: part s is the
+// product of A's and B's K range [s*ks, min(K, (s+1)*ks)) into fp32 slice s
+// of the caller's workspace), then one reduction kernel adds the slices in a
+// fixed order (slice 0 first) and writes C in the output type.  Both launches
+// are enqueued on the caller's stream; the library allocates nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tgemm.h"
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// Part geometry: ks k-elements per part (a multiple of 8, so every part's A
+// and B bases stay 16-byte aligned), `parts` parts (the last may be
+// shorter), workspace rows of ldw = N rounded up to 8 floats.
+struct Parts {
+  int64_t ks, parts, ldw;
+};
+Parts parts_of(const gemm_plan_t& p, int32_t splits) {
+  Parts r;
+  r.ks = p.k > 0 ? round_up(cdiv(p.k, splits), 8) : 0;
+  r.parts = p.k > 0 ? cdiv(p.k, r.ks) : 0;
+  r.ldw = round_up(p.n > 0 ? p.n : 1, 8);
+  return r;
+}
+
+// C[i][j] = sum over parts s (in order) of W[s][i][j], rounded to Out.
+// Thread q handles 4 consecutive columns of one row: one 16-byte load per
+// part (ldw and the slice stride are multiples of 4 floats, so the loads are
+// aligned; columns N .. ldw-1 are read but never stored).
+template <typename Out>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ W, int64_t slice, int32_t parts,
+                                                            int64_t M, int64_t N, int64_t ldw, Out* __restrict__ C,
+                                                            int64_t ldc) {
+  const int64_t groups = (N + 3) / 4;
+  const int64_t total = M * groups;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total; q += (int64_t)gridDim.x * 256) {
+    const int64_t i = q / groups, j = (q - i * groups) * 4;
+    const float* w = W + i * ldw + j;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int32_t p = 0; p < parts; ++p) {
+      const f32x4 v = *(const f32x4*)(w + p * slice);
+      s[0] += v[0];
+      s[1] += v[1];
+      s[2] += v[2];
+      s[3] += v[3];
+    }
+    Out* c = C + i * ldc + j;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (j + e < N) c[e] = (Out)s[e];  // nearest, ties to even, for 16-bit outputs
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+uint64_t tg_splitk_workspace_bytes(const gemm_plan_t* plan, int32_t splits) {
+  if (!plan || plan->abi_version != TG_ABI_VERSION || splits < 1 || splits > TG_SPLITK_MAX) return 0;
+  const Parts g = parts_of(*plan, splits);
+  const double bytes = 4.0 * (double)g.parts * (double)plan->m * (double)g.ldw;
+  if (bytes >= 4.0e18) return 0;
+  return (uint64_t)g.parts * (uint64_t)plan->m * (uint64_t)g.ldw * 4u;
+}
+
+int32_t tg_splitk_choose(const gemm_plan_t* plan) {
+  if (!plan || plan->abi_version != TG_ABI_VERSION) return 1;
+  const gemm_plan_t& p = *plan;
+  // 128 x 128 tiles; aim at two work items per CU of MI355X's 256, with
+  // parts of at least 512 k (shorter parts make the workspace traffic
+  // comparable to the product's own)
+  const int64_t tiles = cdiv(p.m, 128) * cdiv(p.n, 128);
+  if (tiles == 0 || tiles >= 128 || p.k < 2048) return 1;
+  int64_t s = cdiv(512, tiles);
+  if (s > p.k / 512) s = p.k / 512;
+  if (s > TG_SPLITK_MAX) s = TG_SPLITK_MAX;
+  return (int32_t)(s < 1 ? 1 : s);
+}
+
+tg_status gemm_splitk_run(const gemm_plan_t* plan, int32_t splits, void* workspace, uint64_t workspace_bytes,
+                          const void* A, const void* B, void* C, hipStream_t stream) {
+  if (!plan || plan->abi_version != TG_ABI_VERSION) return TG_ERR_INVALID;
+  if (splits < 1 || splits > TG_SPLITK_MAX) return TG_ERR_INVALID;
+  const gemm_plan_t& p = *plan;
+  if (p.in_type < 0 || p.in_type > 1 || (p.out_type != TG_FP32 && p.out_type != p.in_type)) return TG_ERR_INVALID;
+  if (p.m == 0 || p.n == 0) return TG_OK;
+  if (!C) return TG_ERR_INVALID;
+  if (p.k > 0 && (!A || !B)) return TG_ERR_INVALID;
+  const Parts g = parts_of(p, splits);
+  const uint64_t need = tg_splitk_workspace_bytes(plan, splits);
+  if (p.k > 0 && (need == 0 || !workspace || workspace_bytes < need || (uintptr_t)workspace % 16 != 0))
+    return TG_ERR_INVALID;
+
+  float* W = static_cast<float*>(workspace);
+  const int64_t slice = p.m * g.ldw;  // floats per part
+  if (g.parts > 0) {
+    gemm_group_problem_t probs[TG_SPLITK_MAX];
+    const char* a = static_cast<const char*>(A);
+    const char* b = static_cast<const char*>(B);
+    for (int64_t s = 0; s < g.parts; ++s) {
+      const int64_t k0 = s * g.ks;
+      gemm_group_problem_t& q = probs[s];
+      q.m = p.m;
+      q.n = p.n;
+      q.k = (p.k - k0 < g.ks) ? p.k - k0 : g.ks;
+      q.lda = p.lda;
+      q.ldb = p.ldb;
+      q.ldc = g.ldw;
+      // K runs along A's rows when A is stored M x K, down its rows when stored K x M; likewise B
+      q.A = a + 2 * (p.trans_a ? k0 * p.lda : k0);
+      q.B = b + 2 * (p.trans_b ? k0 : k0 * p.ldb);
+      q.C = W + s * slice;
+    }
+    const tg_status st =
+        gemm_group_run((tg_dtype)p.in_type, TG_FP32, p.trans_a, p.trans_b, probs, g.parts, -1, stream);
+    if (st != TG_OK) return st;
+  }
+  const int64_t total = p.m * cdiv(p.n, 4);
+  const int64_t blocks64 = cdiv(total, 256);
+  const unsigned blocks = (unsigned)(blocks64 < 8192 ? blocks64 : 8192);
+  const int32_t parts = (int32_t)g.parts;
+  if (p.out_type == TG_FP32)
+    hipLaunchKernelGGL(splitk_reduce_kernel<float>, dim3(blocks), dim3(256), 0, stream, W, slice, parts, p.m, p.n,
+                       g.ldw, static_cast<float*>(C), p.ldc);
+  else if (p.out_type == TG_BF16)
+    hipLaunchKernelGGL(splitk_reduce_kernel<__bf16>, dim3(blocks), dim3(256), 0, stream, W, slice, parts, p.m, p.n,
+                       g.ldw, static_cast<__bf16*>(C), p.ldc);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<_Float16>, dim3(blocks), dim3(256), 0, stream, W, slice, parts, p.m,
+                       p.n, g.ldw, static_cast<_Float16*>(C), p.ldc);
+  return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
+}
+
+}  // extern "C"

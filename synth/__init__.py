@@ -174,6 +174,15 @@ def square_8192(seed: int = 4, out_dtype: str = "bf16") -> List[Problem]:
     return [Problem("square_8192_nn", A, B, 0, 0, 8192, 8192, 8192, out_dtype=out_dtype)]
 
 
+def long_k(seed: int = 10, m: int = 1024, n: int = 1024, k: int = 65536, out_dtype: str = "bf16") -> List[Problem]:
+    """A product with few output tiles and a long K (64 tiles of 128 x 128 on
+    256 compute units): the shape split-K exists for."""
+    rng = np.random.default_rng(seed)
+    A = draw(rng, (m, k), "normal", 1.0)
+    B = draw(rng, (k, n), "normal", 1.0)
+    return [Problem(f"long_k_{m}x{n}x{k}_nn", A, B, 0, 0, m, n, k, out_dtype=out_dtype)]
+
+
 @dataclasses.dataclass
 class AttnProblem:
     """O = softmax(scale * Q K^T) V for ``batch`` heads, row-major with the head

@@ -27,7 +27,8 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"gemm_plan", "bmm_plan", "gemm_plan_tile", "gemm_run", "bmm_run", "tg_status_str", "tg_abi_version",
-            "tg_variant_tiles", "attention_fwd", "gemm_group_run", "tg_group_tiles"} <= set(names)
+            "tg_variant_tiles", "attention_fwd", "gemm_group_run", "tg_group_tiles", "gemm_splitk_run",
+            "tg_splitk_workspace_bytes", "tg_splitk_choose"} <= set(names)
     L = tg.lib()
     for n in names:
         assert hasattr(L, n), f"libtgemm.so does not export {n}"
@@ -345,5 +346,53 @@ def test_python_constants_match_the_header():
     assert int(defs["TG_TILE_PINGPONG"], 0) == tg.TILE_PINGPONG
     assert int(defs["TG_TILE_PINGPONG_EPI"], 0) == tg.TILE_PINGPONG_EPI
     assert int(defs["TG_TILE_PANEL"], 0) == tg.TILE_PANEL
+    assert int(defs["TG_SPLITK_MAX"], 0) == tg.SPLITK_MAX
     for name in ("EVEN_K", "VEC16", "ROTATE_K", "PERSIST", "PREFETCH", "STREAM_C"):
         assert int(defs["TG_FLAG_" + name], 0) == getattr(tg, "FLAG_" + name)
+
+
+def test_splitk_host_side():
+    """Workspace size, split suggestion and argument checks of gemm_splitk_run
+    (all answered on the host, before anything is enqueued)."""
+    import torch
+    L = tg.lib()
+    p = tg.plan(1024, 1000, 65536, out_dtype=torch.bfloat16)
+    # ks = ceil(65536 / 8) = 8192 -> 8 parts of 1024 rows x ldw = 1000 rounded up to 8 floats
+    assert tg.splitk_workspace_bytes(p, 8) == 8 * 1024 * 1000 * 4
+    # K = 1000 in 3 parts: ks = 336 (a multiple of 8) -> parts of 336, 336, 328
+    q = tg.plan(64, 36, 1000)
+    assert tg.splitk_workspace_bytes(q, 3) == 3 * 64 * 40 * 4
+    # more splits than 8-element parts: K = 24 in 8 splits -> ks = 8, 3 parts
+    r = tg.plan(16, 16, 24)
+    assert tg.splitk_workspace_bytes(r, 8) == 3 * 16 * 16 * 4
+    assert tg.splitk_workspace_bytes(tg.plan(16, 16, 0), 4) == 0
+    for bad in (0, -1, tg.SPLITK_MAX + 1):
+        assert tg.splitk_workspace_bytes(p, bad) == 0
+    # suggestion: 64 tiles of 128 x 128 and a long K -> 8 parts (two items per CU); many tiles or short K -> 1
+    assert tg.splitk_choose(p) == 8
+    assert tg.splitk_choose(tg.plan(1024, 1024, 1024)) == 1
+    assert tg.splitk_choose(tg.plan(4096, 4096, 65536)) == 1
+    assert tg.splitk_choose(tg.plan(128, 128, 4096)) == 8  # K / 512
+    assert tg.splitk_choose(tg.plan(128, 128, 1 << 20)) == tg.SPLITK_MAX
+    stale = tg.GemmPlan.from_buffer_copy(p)
+    stale.abi_version = 0
+    assert tg.splitk_choose(stale) == 1 and tg.splitk_workspace_bytes(stale, 2) == 0
+    A = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails its checks first
+    need = tg.splitk_workspace_bytes(p, 8)
+    ws = ctypes.c_void_p(1 << 24)
+    calls = [
+        (stale, 8, ws, need, A, A, A),          # stale plan
+        (p, 0, ws, need, A, A, A),              # splits out of range
+        (p, tg.SPLITK_MAX + 1, ws, need, A, A, A),
+        (p, 8, ws, need - 1, A, A, A),          # workspace too small
+        (p, 8, None, need, A, A, A),            # no workspace
+        (p, 8, ctypes.c_void_p((1 << 24) + 4), need, A, A, A),  # misaligned workspace
+        (p, 8, ws, need, None, A, A),           # null A with K > 0
+        (p, 8, ws, need, A, A, None),           # null C
+    ]
+    for pl, s, w, nb, a, b, c in calls:
+        assert L.gemm_splitk_run(ctypes.byref(pl), s, w, nb, a, b, c, None) == tg.TG_ERR_INVALID
+    assert L.gemm_splitk_run(None, 8, ws, need, A, A, A, None) == tg.TG_ERR_INVALID
+    # an empty product enqueues nothing
+    e = tg.plan(0, 16, 64)
+    assert L.gemm_splitk_run(ctypes.byref(e), 2, None, 0, None, None, None, None) == tg.TG_OK
