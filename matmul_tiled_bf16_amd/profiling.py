@@ -30,12 +30,19 @@ from collections import defaultdict
 HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30  # bytes read and written by one calibration copy
 
+def _gemm_source(f: str) -> bool:
+    """Sources of the GEMM kernels and their launcher: everything but the fused
+    attention and the split-K driver (host code plus its reduction kernel)."""
+    b = os.path.basename(f)
+    return not b.startswith("attention") and b != "splitk.hip"
+
+
 # kernel families: the kernels' name patterns and the sources they are built from
 FAMILIES = {
     "gemm": (("tile_gemm_kernel", "pingpong_gemm_kernel", "panel_gemm_kernel", "skinny_gemm_kernel",
               "generic_gemm_kernel"),
-             lambda f: not os.path.basename(f).startswith("attention")),
-    "group": (("group_gemm_kernel",), lambda f: not os.path.basename(f).startswith("attention")),
+             lambda f: _gemm_source(f)),
+    "group": (("group_gemm_kernel",), lambda f: _gemm_source(f)),
     "attention": (("attn_fwd_kernel",),
                   lambda f: os.path.basename(f) in ("attention.hpp", "attention.hip", "tile_gemm.hpp",
                                                     "common.hpp")),
