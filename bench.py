@@ -75,6 +75,7 @@ def main():
     ap.add_argument("--tile", type=int, default=None, help="override the planner's tile (same variant)")
     ap.add_argument("--no-persist", action="store_true", help="clear the plan's persistent-launch flags")
     ap.add_argument("--no-prefetch", action="store_true", help="clear the plan's prefetch flag")
+    ap.add_argument("--no-rotate-k", action="store_true", help="clear the plan's rotated-K-walk flag")
     ap.add_argument("--prefetch", action="store_true", help="set the plan's persistent and prefetch flags")
     ap.add_argument("--stream-c", type=int, default=-1, help="force the plan's non-temporal C flag (0/1)")
     ap.add_argument("--group-tile", type=int, default=-1, help="force the grouped launch's tile (group_moe)")
@@ -151,6 +152,8 @@ def main():
             pl.flags &= ~(tg.FLAG_PERSIST | tg.FLAG_PREFETCH)
         if args.no_prefetch:
             pl.flags &= ~tg.FLAG_PREFETCH
+        if args.no_rotate_k:
+            pl.flags &= ~tg.FLAG_ROTATE_K
         if args.prefetch:
             pl.flags |= tg.FLAG_PERSIST | tg.FLAG_PREFETCH
         if args.stream_c == 0:
