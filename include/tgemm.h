@@ -225,16 +225,18 @@ int32_t tg_group_tiles(void);
  * persistent / stream-K family of schedules, for when the tile grid alone
  * leaves compute units idle).  Part s covers k in [s*ks, min(K, (s+1)*ks)),
  * ks = ceil(K / splits) rounded up to a multiple of 8, so there are
- * ceil(K / ks) <= splits parts.  Two launches are enqueued on `stream`:
- *   1. one grouped launch (gemm_group_run) computes each part as an
- *      independent product into fp32 slice s of `workspace`, which is laid
- *      out as parts x m rows of ldw = n rounded up to 8 floats;
- *   2. a reduction adds the slices in a fixed order (slice 0 first) and
+ * ceil(K / ks) <= splits parts.  Enqueued on `stream`:
+ *   1. the parts of exactly ks as one batched product (bmm_plan + bmm_run,
+ *      the batch strides stepping along K), each into fp32 slice s of
+ *      `workspace`, which is laid out as parts x m rows of ldw = n rounded
+ *      up to 8 floats; a shorter last part as one more product (gemm_plan +
+ *      gemm_run) into the last slice;
+ *   2. a reduction that adds the slices in a fixed order (slice 0 first) and
  *      writes C in the plan's output type (nearest-even for 16-bit outputs).
  * The result is deterministic.  It equals gemm_run's up to the order of
  * fp32 additions, and bit for bit where every partial sum is exact.  The
- * plan's variant and tile are not used (the grouped launch picks its own);
- * its types, transposes, sizes and leading dimensions are.
+ * plan's variant and tile are not used (the parts are planned for their own
+ * shape); its types, transposes, sizes and leading dimensions are.
  *   splits: 1 .. TG_SPLITK_MAX (tg_splitk_choose suggests one).
  *   workspace: caller-owned device memory of at least
  *     tg_splitk_workspace_bytes(plan, splits) bytes, 16-byte aligned; it is
@@ -245,7 +247,8 @@ int32_t tg_group_tiles(void);
  * The library allocates nothing.  Returns TG_OK (m = 0 or n = 0: nothing
  * enqueued), TG_ERR_INVALID (null or stale plan, splits out of range, a
  * null pointer with nonzero extents, a workspace too small or misaligned),
- * TG_ERR_UNSUPPORTED or TG_ERR_HIP as gemm_group_run does.
+ * TG_ERR_UNSUPPORTED or TG_ERR_HIP as bmm_run does.  All checks run before
+ * anything is enqueued.
  */
 #define TG_SPLITK_MAX 32
 tg_status gemm_splitk_run(const gemm_plan_t* plan, int32_t splits, void* workspace, uint64_t workspace_bytes,
@@ -256,9 +259,10 @@ tg_status gemm_splitk_run(const gemm_plan_t* plan, int32_t splits, void* workspa
 uint64_t tg_splitk_workspace_bytes(const gemm_plan_t* plan, int32_t splits);
 
 /* A split count for `plan`: 1 (do not split) unless the product has fewer
- * than 128 output tiles of 128 x 128 and K >= 2048; then enough parts to give
- * MI355X's 256 CUs two work items each, with parts of at least 512 k and at
- * most TG_SPLITK_MAX parts.  Host-only; 1 for an invalid plan. */
+ * than 128 output tiles of 256 x 256 (the ping-pong kernel's) and K >= 2048;
+ * then enough parts to give MI355X's 256 CUs one such work item each, with
+ * parts of at least 512 k and at most TG_SPLITK_MAX parts.  Host-only; 1 for
+ * an invalid plan. */
 int32_t tg_splitk_choose(const gemm_plan_t* plan);
 
 /*

@@ -4,11 +4,14 @@
 // persistent / stream-K family of schedules for when the tile grid alone
 // leaves compute units idle).
 //
-// The parts go out as one grouped launch (gemm_group_run: part s is the
-// product of A's and B's K range [s*ks, min(K, (s+1)*ks)) into fp32 slice s
-// of the caller's workspace), then one reduction kernel adds the slices in a
-// fixed order (slice 0 first) and writes C in the output type.  Both launches
-// are enqueued on the caller's stream; the library allocates nothing.
+// The parts of equal length go out as one batched product (bmm_plan +
+// bmm_run: part s reads A's and B's K range [s*ks, (s+1)*ks) through batch
+// strides and writes fp32 slice s of the caller's workspace), a shorter last
+// part as one more product, and one reduction kernel adds the slices in a
+// fixed order (slice 0 first) and writes C in the output type.  The batched
+// product gets the planner's kernel for its shape -- the ping-pong kernel
+// once the parts make 128 or more of its 256x256 work items.  Every launch
+// goes on the caller's stream; the library allocates nothing.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -78,12 +81,13 @@ uint64_t tg_splitk_workspace_bytes(const gemm_plan_t* plan, int32_t splits) {
 int32_t tg_splitk_choose(const gemm_plan_t* plan) {
   if (!plan || plan->abi_version != TG_ABI_VERSION) return 1;
   const gemm_plan_t& p = *plan;
-  // 128 x 128 tiles; aim at two work items per CU of MI355X's 256, with
-  // parts of at least 512 k (shorter parts make the workspace traffic
-  // comparable to the product's own)
-  const int64_t tiles = cdiv(p.m, 128) * cdiv(p.n, 128);
+  // 256 x 256 tiles (the ping-pong kernel's): a product with 128 or more of
+  // them already runs on that kernel whole; otherwise aim at one work item
+  // per CU of MI355X's 256, with parts of at least 512 k (shorter parts make
+  // the workspace traffic comparable to the product's own)
+  const int64_t tiles = cdiv(p.m, 256) * cdiv(p.n, 256);
   if (tiles == 0 || tiles >= 128 || p.k < 2048) return 1;
-  int64_t s = cdiv(512, tiles);
+  int64_t s = cdiv(256, tiles);
   if (s > p.k / 512) s = p.k / 512;
   if (s > TG_SPLITK_MAX) s = TG_SPLITK_MAX;
   return (int32_t)(s < 1 ? 1 : s);
@@ -105,26 +109,32 @@ tg_status gemm_splitk_run(const gemm_plan_t* plan, int32_t splits, void* workspa
 
   float* W = static_cast<float*>(workspace);
   const int64_t slice = p.m * g.ldw;  // floats per part
-  if (g.parts > 0) {
-    gemm_group_problem_t probs[TG_SPLITK_MAX];
-    const char* a = static_cast<const char*>(A);
-    const char* b = static_cast<const char*>(B);
-    for (int64_t s = 0; s < g.parts; ++s) {
-      const int64_t k0 = s * g.ks;
-      gemm_group_problem_t& q = probs[s];
-      q.m = p.m;
-      q.n = p.n;
-      q.k = (p.k - k0 < g.ks) ? p.k - k0 : g.ks;
-      q.lda = p.lda;
-      q.ldb = p.ldb;
-      q.ldc = g.ldw;
-      // K runs along A's rows when A is stored M x K, down its rows when stored K x M; likewise B
-      q.A = a + 2 * (p.trans_a ? k0 * p.lda : k0);
-      q.B = b + 2 * (p.trans_b ? k0 : k0 * p.ldb);
-      q.C = W + s * slice;
-    }
-    const tg_status st =
-        gemm_group_run((tg_dtype)p.in_type, TG_FP32, p.trans_a, p.trans_b, probs, g.parts, -1, stream);
+  const char* a = static_cast<const char*>(A);
+  const char* b = static_cast<const char*>(B);
+  // K runs along A's rows when A is stored M x K, down its rows when stored
+  // K x M; likewise B (along its rows when stored N x K)
+  auto a_at = [&](int64_t k0) { return a + 2 * (p.trans_a ? k0 * p.lda : k0); };
+  auto b_at = [&](int64_t k0) { return b + 2 * (p.trans_b ? k0 : k0 * p.ldb); };
+  const tg_dtype in = (tg_dtype)p.in_type;
+  const int64_t full = g.ks > 0 ? p.k / g.ks : 0;  // parts of exactly ks (none when K = 0)
+  const int64_t tail = p.k - full * g.ks;           // a shorter last part (0: none)
+  // both plans are made (and checked) before anything is enqueued
+  gemm_plan_t qf, qt;
+  if (full > 0) {
+    const tg_status st = bmm_plan(&qf, in, TG_FP32, p.trans_a, p.trans_b, p.m, p.n, g.ks, p.lda, p.ldb, g.ldw, full);
+    if (st != TG_OK) return st;
+  }
+  if (tail > 0) {
+    const tg_status st = gemm_plan(&qt, in, TG_FP32, p.trans_a, p.trans_b, p.m, p.n, tail, p.lda, p.ldb, g.ldw);
+    if (st != TG_OK) return st;
+  }
+  if (full > 0) {
+    const int64_t sa = p.trans_a ? g.ks * p.lda : g.ks, sb = p.trans_b ? g.ks : g.ks * p.ldb;
+    const tg_status st = bmm_run(&qf, full, sa, sb, slice, a, b, W, stream);
+    if (st != TG_OK) return st;
+  }
+  if (tail > 0) {
+    const tg_status st = gemm_run(&qt, a_at(full * g.ks), b_at(full * g.ks), W + full * slice, stream);
     if (st != TG_OK) return st;
   }
   const int64_t total = p.m * cdiv(p.n, 4);

@@ -104,7 +104,7 @@ int skinny_choose(int64_t m, int64_t) { return m > 16 ? 1 : 0; }
 // small BLOCK_M).  Work items are tiles times batch matrices.
 //  * MFMA-bound problems (arithmetic intensity above MI355X's ~312 FLOP/B
 //    ridge) take the 256x256 ping-pong kernel (8 waves alternating MFMA and
-//    memory phases) when there are >= 2 items per CU;
+//    memory phases) from 128 work items on;
 //  * HBM-bound ones with K <= 128 and >= 2048 tiles take the panel kernel
 //    (runs of 128x128 tiles along a row panel of C: the next tile's B copy
 //    overlaps this tile's stores);
@@ -120,7 +120,10 @@ int choose_tile(const gemm_plan_t& p, int64_t batch) {
   const double flops = 2.0 * (double)m * (double)n * (double)k;
   const double bytes = 2.0 * ((double)m * k + (double)k * n) + (double)out_size * m * n;
   const bool mfma_bound = bytes > 0 && flops / bytes > 312.5;
-  if (mfma_bound && items(8) >= 512 && k > 0) return tg::kPingPongTile;  // 256x256, 8 waves
+  // 256x256, 8 waves: from 128 work items on (measured: 2048x4096x8192
+  // 0.172 vs 0.194 ms on 128x128 tiles, 4096^2x8192 0.204 vs 0.370 ms; at 64
+  // items, 2048^2x8192, the 128x128 tiles' 256 work-groups win)
+  if (mfma_bound && items(8) >= 128 && k > 0) return tg::kPingPongTile;
   // short K and many tiles: runs along row panels, A held in registers
   if (!mfma_bound && panel_ok(p) && items(tg::kPanelTile) >= 2048) return tg::kPanelTile;
   if (items(13) >= 256) return mfma_bound ? 1 : 13;  // 128x128

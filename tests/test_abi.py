@@ -186,6 +186,10 @@ def test_plan_choices_for_the_workloads():
         tg.plan(64, 64, 64, batch=0)
     p = tg.plan(8192, 8192, 8192, out_dtype=torch.bfloat16)
     assert (p.variant, p.bm, p.bn, p.wg_threads) == (tg.VARIANT_TILE, 256, 256, 512) and p.tiles_m * p.tiles_n == 1024
+    # MFMA-bound products take the ping-pong kernel from 128 of its 256 x 256 work items on
+    assert tg.plan(2048, 4096, 8192, out_dtype=torch.bfloat16).tile == tg.TILE_PINGPONG  # 128 items
+    assert tg.plan(1024, 1024, 4096, batch=16).tile == tg.TILE_PINGPONG                # 16 x 16 items
+    assert tg.plan(2048, 2048, 8192, out_dtype=torch.bfloat16).tile == 1                # 64 items: 128 x 128
     assert p.flags & tg.FLAG_PERSIST and p.flags & tg.FLAG_PREFETCH  # MFMA-bound: prefetch during stores
     assert p.workspace_bytes == 0
 
@@ -368,10 +372,11 @@ def test_splitk_host_side():
     assert tg.splitk_workspace_bytes(tg.plan(16, 16, 0), 4) == 0
     for bad in (0, -1, tg.SPLITK_MAX + 1):
         assert tg.splitk_workspace_bytes(p, bad) == 0
-    # suggestion: 64 tiles of 128 x 128 and a long K -> 8 parts (two items per CU); many tiles or short K -> 1
-    assert tg.splitk_choose(p) == 8
+    # suggestion: 16 tiles of 256 x 256 and a long K -> 16 parts (one item per CU); many tiles or short K -> 1
+    assert tg.splitk_choose(p) == 16
     assert tg.splitk_choose(tg.plan(1024, 1024, 1024)) == 1
     assert tg.splitk_choose(tg.plan(4096, 4096, 65536)) == 1
+    assert tg.splitk_choose(tg.plan(2048, 2048, 65536)) == 4  # 64 tiles of 256 x 256
     assert tg.splitk_choose(tg.plan(128, 128, 4096)) == 8  # K / 512
     assert tg.splitk_choose(tg.plan(128, 128, 1 << 20)) == tg.SPLITK_MAX
     stale = tg.GemmPlan.from_buffer_copy(p)

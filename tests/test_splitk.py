@@ -1,7 +1,8 @@
 """Split-K products (gemm_splitk_run) against the oracle.
 
-Parts of K run as one grouped launch into an fp32 workspace, then a fixed-order
-reduction writes C.  Covered here:
+The parts of K run as one batched product (plus one product for a shorter
+last part) into an fp32 workspace, then a fixed-order reduction writes C.
+Covered here:
 - every transpose, with uneven parts (the last part shorter);
 - more splits than 8-element parts;
 - M/N tails, including N not a multiple of 4 (scalar tail of the reduction);
@@ -109,15 +110,16 @@ def test_k_zero_writes_zeros_without_workspace():
 
 
 def test_long_k_at_the_suggested_split():
-    """1024 x 1024 x 65536, NN, bf16 out: 64 output tiles, so the suggested
-    split gives 8 parts; sampled against the oracle."""
+    """1024 x 1024 x 65536, NN, bf16 out: 16 output tiles of 256 x 256, so the
+    suggested split gives 16 parts (the batched product runs on the ping-pong
+    kernel); sampled against the oracle."""
     m, n, k = 1024, 1024, 65536
     idx = synth.sample_indices(9, 1, m, n, count=1024)
     rng = np.random.default_rng(9)
     A = synth.draw(rng, (m, k), "normal", 1.0)
     B = synth.draw(rng, (k, n), "normal", 1.0)
     p = tg.plan(m, n, k, out_dtype=torch.bfloat16)
-    assert tg.splitk_choose(p) == 8
+    assert tg.splitk_choose(p) == 16
     C = tg.gemm_splitk(to_gpu(A), to_gpu(B), out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     got = values(C)[idx[:, 1], idx[:, 2]]
