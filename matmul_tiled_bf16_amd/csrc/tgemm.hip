@@ -127,6 +127,9 @@ int choose_tile(const gemm_plan_t& p, int64_t batch) {
   // short K and many tiles: runs along row panels, A held in registers
   if (!mfma_bound && panel_ok(p) && items(tg::kPanelTile) >= 2048) return tg::kPanelTile;
   if (items(13) >= 256) return mfma_bound ? 1 : 13;  // 128x128
+  // MFMA-bound with more than 128 of them: still 128x128 (1536^2 x 8192: 86
+  // vs 97 us on 64x64 tiles; at 128 items, 1024x2048x8192, 64x64 wins 61 vs 87)
+  if (mfma_bound && items(13) > 128) return 1;
   // 64x64: with a long K the 4-deep ring keeps three steps' copies in flight
   // (1000^3: 12.3 -> 11.1 us); with a short one the 2-deep ring's shorter
   // prologue wins (256^3: 5.5 vs 5.9 us)

@@ -190,6 +190,8 @@ def test_plan_choices_for_the_workloads():
     assert tg.plan(2048, 4096, 8192, out_dtype=torch.bfloat16).tile == tg.TILE_PINGPONG  # 128 items
     assert tg.plan(1024, 1024, 4096, batch=16).tile == tg.TILE_PINGPONG                # 16 x 16 items
     assert tg.plan(2048, 2048, 8192, out_dtype=torch.bfloat16).tile == 1                # 64 items: 128 x 128
+    assert tg.plan(1536, 1536, 8192, out_dtype=torch.bfloat16).tile == 1                # 144 128 x 128 items
+    assert tg.plan(1024, 2048, 8192, out_dtype=torch.bfloat16).tile == 26               # 128: the 64 x 64 ring
     assert p.flags & tg.FLAG_PERSIST and p.flags & tg.FLAG_PREFETCH  # MFMA-bound: prefetch during stores
     assert p.workspace_bytes == 0
 
