@@ -9,6 +9,8 @@ It is forced onto shapes that exercise every path of it:
 - Batches with padded ldc.
 - Runs split over a row panel, including a last run shorter than the rest.
 - Integer inputs, which must match bit for bit.
+- Batches that share an operand through a zero batch stride, for the panel
+  kernel and for the tile kernel's non-temporal loads of unshared operands.
 - Every case the launcher hands to the 128 x 128 tile kernel instead: an
   epilogue, A stored K x M, K > 128, K = 0, and N not a whole number of
   16-byte output units.
@@ -125,3 +127,28 @@ def test_epilogue_goes_to_the_tile_kernel():
     torch.cuda.synchronize()
     P = oracle.gemm(A, B, m=m, n=n, k=k)
     check_exact(values(Cg), oracle.epilogue(P, 2.0, -1.0, C0.astype(np.float64), None), "fp32", "panel epilogue")
+
+
+@pytest.mark.parametrize("case", ["panel_shared_B", "one_column_shared_A", "one_column_own_A"])
+def test_batches_that_share_an_operand(case):
+    """A zero batch stride shares one operand between the batch's products.
+    The panel kernel reads it per run. With one column of tiles, the launcher
+    loads A non-temporally only when no other matrix of the batch reads it."""
+    rng = np.random.default_rng(41)
+    batch = 3
+    if case == "panel_shared_B":
+        m, n, k, tb, tile = 264, 640, 128, 1, tg.TILE_PANEL
+        A = synth.draw(rng, (batch, m, k), "int", -4, 4)
+        B = synth.draw(rng, (n, k), "int", -4, 4)
+        sA, sB = m * k, 0
+    else:
+        m, n, k, tb, tile = 520, 128, 1000, 0, 13
+        A = synth.draw(rng, (m, k) if case == "one_column_shared_A" else (batch, m, k), "int", -4, 4)
+        B = synth.draw(rng, (batch, k, n), "int", -4, 4)
+        sA, sB = (0 if case == "one_column_shared_A" else m * k), k * n
+    pl = tg.plan_tile(tg.plan(m, n, k, trans_b=tb, batch=batch), tg.VARIANT_TILE, tile)
+    C = torch.empty((batch, m, n), dtype=torch.float32, device="cuda")
+    tg.bmm_run(pl, batch, sA, sB, m * n, to_gpu(A), to_gpu(B), C)
+    torch.cuda.synchronize()
+    ref = oracle.gemm(A, B, m=m, n=n, k=k, trans_b=tb, batch=batch, stride_a=sA, stride_b=sB)
+    check_exact(values(C), ref, "fp32", case)
