@@ -258,11 +258,13 @@ tg_status gemm_splitk_run(const gemm_plan_t* plan, int32_t splits, void* workspa
  * (parts * m * ldw * 4); 0 for an invalid plan or split count, or K = 0. */
 uint64_t tg_splitk_workspace_bytes(const gemm_plan_t* plan, int32_t splits);
 
-/* A split count for `plan`: 1 (do not split) unless the product has fewer
- * than 128 output tiles of 256 x 256 (the ping-pong kernel's) and K >= 2048;
- * then enough parts to give MI355X's 256 CUs one such work item each, with
- * parts of at least 512 k and at most TG_SPLITK_MAX parts.  Host-only; 1 for
- * an invalid plan. */
+/* A split count for `plan`, counted in output tiles of 256 x 256 (the
+ * ping-pong kernel's).  1 (do not split) when the product has 128 or more of
+ * them or K < 2048.  Otherwise the most parts that fit one round of MI355X's
+ * 256 CUs with parts at least 2048 deep, if that makes 144 or more work
+ * items; else, for outputs of at most 16 such tiles, enough parts for 256
+ * items with parts at least 512 deep; else 1.  At most TG_SPLITK_MAX.
+ * Host-only; 1 for an invalid plan. */
 int32_t tg_splitk_choose(const gemm_plan_t* plan);
 
 /*

@@ -81,13 +81,20 @@ uint64_t tg_splitk_workspace_bytes(const gemm_plan_t* plan, int32_t splits) {
 int32_t tg_splitk_choose(const gemm_plan_t* plan) {
   if (!plan || plan->abi_version != TG_ABI_VERSION) return 1;
   const gemm_plan_t& p = *plan;
-  // 256 x 256 tiles (the ping-pong kernel's): a product with 128 or more of
-  // them already runs on that kernel whole; otherwise aim at one work item
-  // per CU of MI355X's 256, with parts of at least 512 k (shorter parts make
-  // the workspace traffic comparable to the product's own)
+  // Counted in 256 x 256 tiles (the ping-pong kernel's): a product with 128
+  // or more of them already runs on that kernel whole.  Otherwise one round
+  // of work items on MI355X's 256 CUs with parts at least 2048 deep, if that
+  // gives 144 or more items (with fewer, the plain launch's smaller tiles
+  // measured as fast); tiny outputs (<= 16 such tiles, which a plain launch
+  // leaves almost serial) split further, down to parts of 512.
   const int64_t tiles = cdiv(p.m, 256) * cdiv(p.n, 256);
   if (tiles == 0 || tiles >= 128 || p.k < 2048) return 1;
-  int64_t s = cdiv(256, tiles);
+  int64_t s = 256 / tiles;
+  if (s > p.k / 2048) s = p.k / 2048;
+  if (s > TG_SPLITK_MAX) s = TG_SPLITK_MAX;
+  if (s >= 2 && tiles * s >= 144) return (int32_t)s;
+  if (tiles > 16) return 1;
+  s = cdiv(256, tiles);
   if (s > p.k / 512) s = p.k / 512;
   if (s > TG_SPLITK_MAX) s = TG_SPLITK_MAX;
   return (int32_t)(s < 1 ? 1 : s);

@@ -379,6 +379,9 @@ def test_splitk_host_side():
     assert tg.splitk_choose(tg.plan(1024, 1024, 1024)) == 1
     assert tg.splitk_choose(tg.plan(4096, 4096, 65536)) == 1
     assert tg.splitk_choose(tg.plan(2048, 2048, 65536)) == 4  # 64 tiles of 256 x 256
+    assert tg.splitk_choose(tg.plan(1536, 1536, 8192)) == 4   # 36 tiles: 144 items of 2048-deep parts
+    assert tg.splitk_choose(tg.plan(2048, 2048, 4096)) == 1   # only 128 items of 2048-deep parts
+    assert tg.splitk_choose(tg.plan(1024, 2048, 8192)) == 1
     assert tg.splitk_choose(tg.plan(128, 128, 4096)) == 8  # K / 512
     assert tg.splitk_choose(tg.plan(128, 128, 1 << 20)) == tg.SPLITK_MAX
     stale = tg.GemmPlan.from_buffer_copy(p)
