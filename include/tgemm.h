@@ -67,9 +67,9 @@ typedef enum {
  * large MFMA-bound problems.  TG_TILE_PINGPONG_EPI is the same kernel with the
  * alpha/beta/bias epilogue compiled in; the run calls use whichever of the two
  * matches the call (with or without an epilogue), and the 8-wave tile kernel
- * (entry 8) when K = 0. */
-#define TG_TILE_PINGPONG 23
-#define TG_TILE_PINGPONG_EPI 24
+ * (entry 3) when K = 0. */
+#define TG_TILE_PINGPONG 8
+#define TG_TILE_PINGPONG_EPI 9
 
 /* Entry of the TG_VARIANT_TILE table served by the panel kernel, for products
  * with a short K whose time goes into writing C ("Triton Optimization
@@ -79,8 +79,8 @@ typedef enum {
  * lds_bytes = 2 * bk * bn * 2 with bk = 128, the largest K it takes.  It
  * serves A stored M x K, 0 < K <= 128, N a multiple of 16 bytes' worth of
  * output elements, and no epilogue.  The run calls send any other call
- * planned on this entry to the 128 x 128 tile kernel (entry 13). */
-#define TG_TILE_PANEL 25
+ * planned on this entry to the 128 x 128 tile kernel (entry 4). */
+#define TG_TILE_PANEL 10
 
 /* plan.flags bits */
 #define TG_FLAG_EVEN_K 0x1 /* K is a multiple of the K-tile: no masked K step */

@@ -24,8 +24,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "tgemm.h")
 TG_BF16, TG_FP16, TG_FP32 = 0, 1, 2
 TG_OK, TG_ERR_INVALID, TG_ERR_UNSUPPORTED, TG_ERR_HIP = 0, 1, 2, 3
 VARIANT_GENERIC, VARIANT_TILE, VARIANT_SKINNY = 0, 1, 2
-TILE_PINGPONG, TILE_PINGPONG_EPI = 23, 24  # TG_TILE_PINGPONG, TG_TILE_PINGPONG_EPI
-TILE_PANEL = 25  # TG_TILE_PANEL
+TILE_PINGPONG, TILE_PINGPONG_EPI = 8, 9  # TG_TILE_PINGPONG, TG_TILE_PINGPONG_EPI
+TILE_PANEL = 10  # TG_TILE_PANEL
 SPLITK_MAX = 32  # TG_SPLITK_MAX
 FLAG_EVEN_K, FLAG_VEC16, FLAG_ROTATE_K, FLAG_PERSIST, FLAG_PREFETCH, FLAG_STREAM_C = 0x1, 0x2, 0x4, 0x8, 0x10, 0x20
 
@@ -226,15 +226,40 @@ def bmm_run_ex(p: GemmPlan, batch: int, stride_a: int, stride_b: int, stride_c: 
         raise TgError(st, "bmm_run_ex")
 
 
-def _check_matrix(X, name):
+def _check_matrix(X, name, dims=(2,), out=False):
+    """Validate a row-major operand before anything reaches the library.
+
+    The kernels address element (r, c) of a matrix at base + r*ld + c with
+    ld = stride(-2), so the last dimension must be contiguous and rows must not
+    overlap (stride(-2) >= shape[-1] whenever there are two or more rows);
+    otherwise the kernels would read or write outside the tensor's storage.
+    A 3-D input may share one matrix across the batch (stride(0) = 0); a 3-D
+    output's matrices must not overlap.  Shape checks come first, so they
+    raise the same ValueError with or without a GPU."""
+    if X.dim() not in dims:
+        raise ValueError(f"{name} must be a {' or '.join(f'{d}-D' for d in dims)} tensor, got {X.dim()}-D")
+    rows, cols = X.shape[-2], X.shape[-1]
+    if cols > 1 and X.stride(-1) != 1:
+        raise ValueError(f"{name} must have a contiguous last dimension (stride(-1) = {X.stride(-1)})")
+    if rows > 1 and X.stride(-2) < cols:
+        raise ValueError(f"{name}: rows overlap (stride(-2) = {X.stride(-2)} < {cols} columns)")
+    if out and X.dim() == 3 and X.shape[0] > 1 and rows > 0 and cols > 0:
+        span = (rows - 1) * _ld(X) + cols
+        if X.stride(0) < span:
+            raise ValueError(f"{name}: matrices of the batch overlap (stride(0) = {X.stride(0)} < {span})")
     if not X.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
-    if X.dim() not in (2, 3) or (X.shape[-1] > 1 and X.stride(-1) != 1):
-        raise ValueError(f"{name} must be a 2-D or 3-D tensor with a contiguous last dimension")
 
 
 def _ld(X) -> int:
     return max(X.stride(-2), X.shape[-1], 1)
+
+
+def _check_out(out, shape, out_dtype, dims=(2,)):
+    if tuple(out.shape) != tuple(shape) or out.dtype != out_dtype:
+        raise ValueError(f"out has the wrong shape or dtype: {tuple(out.shape)} {out.dtype}, "
+                         f"expected {tuple(shape)} {out_dtype}")
+    _check_matrix(out, "out", dims, out=True)
 
 
 def gemm(A, B, *, trans_a: bool = False, trans_b: bool = False, out_dtype=None, out=None, alpha: float = 1.0,
@@ -255,8 +280,8 @@ def gemm(A, B, *, trans_a: bool = False, trans_b: bool = False, out_dtype=None, 
         raise ValueError("beta != 0 needs `out` (the C to scale)")
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=A.device)
-    elif out.shape != (m, n) or out.dtype != out_dtype:
-        raise ValueError("out has the wrong shape or dtype")
+    else:
+        _check_out(out, (m, n), out_dtype)
     if bias is not None and (bias.dtype != out_dtype or bias.numel() != n or not bias.is_contiguous()):
         raise ValueError("bias must be a contiguous tensor of n values of the output dtype")
     p = plan(m, n, k, trans_a=trans_a, trans_b=trans_b, in_dtype=A.dtype, out_dtype=out_dtype, lda=_ld(A),
@@ -300,8 +325,8 @@ def gemm_splitk(A, B, *, trans_a: bool = False, trans_b: bool = False, out_dtype
     out_dtype = out_dtype or torch.float32
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=A.device)
-    elif out.shape != (m, n) or out.dtype != out_dtype:
-        raise ValueError("out has the wrong shape or dtype")
+    else:
+        _check_out(out, (m, n), out_dtype)
     p = plan(m, n, k, trans_a=trans_a, trans_b=trans_b, in_dtype=A.dtype, out_dtype=out_dtype, lda=_ld(A),
              ldb=_ld(B), ldc=_ld(out))
     splits = splitk_choose(p) if splits is None else int(splits)
@@ -315,10 +340,12 @@ def gemm_splitk(A, B, *, trans_a: bool = False, trans_b: bool = False, out_dtype
 def bmm(A, B, *, trans_a: bool = False, trans_b: bool = False, out_dtype=None, out=None, stream=None):
     """C[b] = op(A[b]) @ op(B[b]) for 3-D tensors [batch, rows, cols] (batch stride from the tensor)."""
     import torch
-    _check_matrix(A, "A")
-    _check_matrix(B, "B")
-    if A.dim() != 3 or B.dim() != 3 or A.shape[0] != B.shape[0]:
-        raise ValueError("A and B must be 3-D with the same batch")
+    _check_matrix(A, "A", (3,))
+    _check_matrix(B, "B", (3,))
+    if A.shape[0] != B.shape[0]:
+        raise ValueError("A and B must have the same batch")
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must have the same dtype")
     batch = A.shape[0]
     m, k = (A.shape[2], A.shape[1]) if trans_a else (A.shape[1], A.shape[2])
     kb, n = (B.shape[2], B.shape[1]) if trans_b else (B.shape[1], B.shape[2])
@@ -327,6 +354,8 @@ def bmm(A, B, *, trans_a: bool = False, trans_b: bool = False, out_dtype=None, o
     out_dtype = out_dtype or torch.float32
     if out is None:
         out = torch.empty((batch, m, n), dtype=out_dtype, device=A.device)
+    else:
+        _check_out(out, (batch, m, n), out_dtype, (3,))
     p = plan(m, n, k, trans_a=trans_a, trans_b=trans_b, in_dtype=A.dtype, out_dtype=out_dtype, lda=_ld(A),
              ldb=_ld(B), ldc=_ld(out), batch=max(batch, 1))
     bmm_run(p, batch, A.stride(0), B.stride(0), out.stride(0), A, B, out, stream)
@@ -350,9 +379,7 @@ def attention(Q, K, V, *, scale: Optional[float] = None, out_dtype=None, out=Non
     import math
     import torch
     for X, name in ((Q, "Q"), (K, "K"), (V, "V")):
-        _check_matrix(X, name)
-        if X.dim() != 3:
-            raise ValueError(f"{name} must be 3-D [batch, rows, head_dim]")
+        _check_matrix(X, name, (3,))
     if not (Q.dtype == K.dtype == V.dtype):
         raise TypeError("Q, K and V must have the same dtype")
     batch, n_q, d = Q.shape
@@ -363,8 +390,8 @@ def attention(Q, K, V, *, scale: Optional[float] = None, out_dtype=None, out=Non
     out_dtype = out_dtype or torch.float32
     if out is None:
         out = torch.empty((batch, n_q, d), dtype=out_dtype, device=Q.device)
-    elif out.shape != (batch, n_q, d) or out.dtype != out_dtype:
-        raise ValueError("out has the wrong shape or dtype")
+    else:
+        _check_out(out, (batch, n_q, d), out_dtype, (3,))
     attention_fwd(_dtype_code(Q.dtype), _dtype_code(out_dtype), batch, n_q, n_k, d, scale, Q, _ld(Q), Q.stride(0),
                   K, _ld(K), K.stride(0), V, _ld(V), V.stride(0), out, _ld(out), out.stride(0), stream)
     return out
@@ -410,9 +437,11 @@ def gemm_group(As, Bs, *, trans_a: bool = False, trans_b: bool = False, out_dtyp
         kb, n = (B.shape[1], B.shape[0]) if trans_b else (B.shape[0], B.shape[1])
         if kb != k:
             raise ValueError(f"problem {i}: inner dimensions differ: {k} vs {kb}")
-        C = outs[i] if outs is not None else torch.empty((m, n), dtype=out_dtype, device=A.device)
-        if C.shape != (m, n) or C.dtype != out_dtype:
-            raise ValueError(f"problem {i}: output has the wrong shape or dtype")
+        if outs is not None:
+            C = outs[i]
+            _check_out(C, (m, n), out_dtype)
+        else:
+            C = torch.empty((m, n), dtype=out_dtype, device=A.device)
         probs.append((m, n, k, _ld(A), _ld(B), _ld(C), A, B, C))
         res.append(C)
     if probs:

@@ -116,24 +116,24 @@ int choose_tile(const gemm_plan_t& p, int64_t batch) {
   const int64_t m = p.m, n = p.n, k = p.k;
   const int out_size = p.out_type == TG_FP32 ? 4 : 2;
   auto items = [&](int t) { return cdiv(m, kTiles[t].bm) * cdiv(n, kTiles[t].bn) * batch; };
-  if (m <= 32) return 5;
+  if (m <= 32) return tg::kThinTile;
   const double flops = 2.0 * (double)m * (double)n * (double)k;
   const double bytes = 2.0 * ((double)m * k + (double)k * n) + (double)out_size * m * n;
   const bool mfma_bound = bytes > 0 && flops / bytes > 312.5;
   // 256x256, 8 waves: from 128 work items on (measured: 2048x4096x8192
   // 0.172 vs 0.194 ms on 128x128 tiles, 4096^2x8192 0.204 vs 0.370 ms; at 64
   // items, 2048^2x8192, the 128x128 tiles' 256 work-groups win)
-  if (mfma_bound && items(8) >= 128 && k > 0) return tg::kPingPongTile;
+  if (mfma_bound && items(tg::kWideTile) >= 128 && k > 0) return tg::kPingPongTile;
   // short K and many tiles: runs along row panels, A held in registers
   if (!mfma_bound && panel_ok(p) && items(tg::kPanelTile) >= 2048) return tg::kPanelTile;
-  if (items(13) >= 256) return mfma_bound ? 1 : 13;  // 128x128
+  if (items(tg::kHbmTile) >= 256) return mfma_bound ? tg::kMfmaMidTile : tg::kHbmTile;  // 128x128
   // MFMA-bound with more than 128 of them: still 128x128 (1536^2 x 8192: 86
   // vs 97 us on 64x64 tiles; at 128 items, 1024x2048x8192, 64x64 wins 61 vs 87)
-  if (mfma_bound && items(13) > 128) return 1;
+  if (mfma_bound && items(tg::kHbmTile) > 128) return tg::kMfmaMidTile;
   // 64x64: with a long K the 4-deep ring keeps three steps' copies in flight
   // (1000^3: 12.3 -> 11.1 us); with a short one the 2-deep ring's shorter
   // prologue wins (256^3: 5.5 vs 5.9 us)
-  return k >= 512 ? 26 : 0;
+  return k >= 512 ? tg::kDeepSmallTile : tg::kSmallTile;
 }
 
 int choose_generic(int64_t m, int64_t n, int64_t batch) { return cdiv(m, 128) * cdiv(n, 128) * batch >= 256 ? 1 : 0; }
@@ -375,12 +375,12 @@ static tg_status launch(const gemm_plan_t* plan, const gemm_epilogue_t* epi, int
   if (pingpong) {
     const int64_t items = cdiv(p.m, kTiles[tile].bm) * cdiv(p.n, kTiles[tile].bn) * batch;
     if (p.k == 0 || items >= ((int64_t)1 << 30))
-      tile = 8;
+      tile = tg::kWideTile;
     else
       tile = a.epi ? tg::kPingPongEpiTile : tg::kPingPongTile;
   }
   // The panel kernel; what it does not serve goes to the 128 x 128 tile.
-  if (variant == TG_VARIANT_TILE && kTiles[tile].kind == tg::kPanel && (a.epi || !panel_ok(p))) tile = 13;
+  if (variant == TG_VARIANT_TILE && kTiles[tile].kind == tg::kPanel && (a.epi || !panel_ok(p))) tile = tg::kHbmTile;
   a.span = 0;
   // Tile kernel: an operand that only one tile of the launch reads -- A when
   // there is one column of tiles, B when there is one row, and neither when
@@ -435,13 +435,8 @@ static tg_status launch(const gemm_plan_t* plan, const gemm_epilogue_t* epi, int
       const int64_t slots = (int64_t)compute_units() * kTiles[tile].occ;
       if (slots > 0 && total >= 2 * slots) {
         cap = slots;
-        const int out_size = p.out_type == TG_FP32 ? 4 : 2;
-        if (p.flags & TG_FLAG_PREFETCH) {
-          if (tg::split_ok(kTiles[tile], out_size) && p.n % (16 / out_size) == 0)
-            a.persist = 2;  // copy waves prefetch, the others store through LDS
-          else if (p.n % 4 == 0 && tg::persist_ok(kTiles[tile]))
-            a.persist = 1;  // every wave prefetches, then stores from registers
-        }
+        if ((p.flags & TG_FLAG_PREFETCH) && p.n % 4 == 0 && tg::persist_ok(kTiles[tile]))
+          a.persist = 1;  // every wave prefetches, then stores from registers
       }
     }
     grid = dim3((unsigned)(total < cap ? total : cap), 1);
@@ -506,8 +501,8 @@ tg_status gemm_group_run(tg_dtype in_type, tg_dtype out_type, int trans_a, int t
       // faster than two work-groups of 64-deep steps on 32 ragged experts)
       gt = 0;  // 64x64
       if (max_m > 32) {
-        if (mfma_bound && items(8) >= 512) gt = 3;       // 256x256, 8 waves
-        else if (items(13) >= 256) gt = mfma_bound ? 2 : 4;
+        if (mfma_bound && items(tg::kWideTile) >= 512) gt = 3;       // 256x256, 8 waves
+        else if (items(tg::kHbmTile) >= 256) gt = mfma_bound ? 2 : 4;
       }
     }
     const TileShape& t = kTiles[kGroupTiles[gt]];

@@ -547,16 +547,7 @@ __device__ __forceinline__ void tile_gemm_body(const KA& kargs) {
   // stores, a fixed count per wave -- stay outstanding.
   constexpr int ST = FM * FN * 4;  // store instructions of store_tile_vec
   constexpr bool PERSIST_OK = (D - 1) * PER_STEP + ST < 64;  // fits the counter
-  // Split mode (args.persist == 2, kernels with dedicated copy waves): the
-  // tile is staged through the ring's LDS and only the waves that issue no
-  // copies store it.  A copy wave's counter then never holds stores, so it
-  // prefetches the next item as soon as the storing waves have read the
-  // staged tile, and no wait of the next item involves the stores at all.
-  constexpr int NS = NW - DW;  // waves that never copy
-  constexpr bool SPLIT_OK =
-      NS > 0 && EPI_PASSES == 1 && ((BM * StagedC<Out, BN>::UPR) % (NS * 64) == 0);
   const bool persist = !GROUP && PERSIST_OK && args.persist == 1 && !args.epi;
-  const bool split = !GROUP && SPLIT_OK && args.persist == 2 && !args.epi;
   // the item being computed: matrix, tile origin, walk rotation, and the
   // source pointers / remaining bytes / K - k0 of the next step to load
   int64_t b = 0, m0 = 0, n0 = 0, rot = 0;
@@ -835,38 +826,6 @@ __device__ __forceinline__ void tile_gemm_body(const KA& kargs) {
     const int64_t cb = b, cm0 = m0, cn0 = n0;
     prefetched = false;
     behind_stores = false;
-    if constexpr (SPLIT_OK) {
-      if (split) {
-        using L = StagedC<Out, BN>;
-        char* Cb = (char*)Cp + cb * args.sC * (int64_t)sizeof(Out);
-        // every wave's reads of the ring are done; stage the tile in it
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        block_barrier();
-        stage_c_write<Out, BM, BN, WM, WN, FM, FN, BM>(lds, 0, wave, lane, acc);
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        block_barrier();
-        if (!copier) {
-          const __amdgpu_buffer_rsrc_t rs =
-              store_rsrc(Cb + (cm0 * ldc + cn0) * (int64_t)L::es, ((M - 1 - cm0) * ldc + (N - cn0)) * (int64_t)L::es);
-          stage_c_store<Out, BN, BM, NS * 64, 0>(lds, rs, ldc, N - cn0, 0, wave * 64 + lane);
-        }
-        // the staged tile has been read (the stores themselves may still be
-        // in flight) before the copy waves refill the ring
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        block_barrier();
-        if (w0 + gridDim.x < total) {
-          setup(w0 + gridDim.x);
-          if (nk > 0) {
-#pragma unroll
-            for (int s = 0; s < D; ++s)
-              if (s < nk) issue((uint32_t)s, std::false_type{});
-          }
-          prefetched = true;
-        }
-        asm volatile("" ::: "memory");
-        continue;
-      }
-    }
     if (persist && w0 + gridDim.x < total) {
       // every wave's LDS reads of this item are done before the ring is
       // refilled with the next item's first stages

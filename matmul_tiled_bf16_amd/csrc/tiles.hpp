@@ -24,54 +24,35 @@ struct TileShape {
   int kind = kTileKernel;
 };
 
+// Only the shapes the planner and the grouped launch choose are built.
 constexpr TileShape kTiles[] = {
-    {64, 64, 64, 2, 2, 2},     // 0: 32x32 per wave -- small and ragged problems
-    {128, 128, 64, 2, 2, 2},   // 1: 64x64 per wave
-    {256, 256, 32, 2, 2, 4},   // 2: 128x128 per wave, 4-deep ring -- large, compute-bound
-    {256, 128, 64, 2, 2, 2},   // 3: 128x64 per wave
-    {128, 256, 64, 2, 2, 2},   // 4: 64x128 per wave
-    {32, 128, 64, 1, 4, 2},    // 5: one 32-row tile -- thin M
-    {128, 128, 32, 2, 2, 4},   // 6: 64x64 per wave, 4-deep ring
-    {256, 256, 64, 2, 2, 2},   // 7: 128x128 per wave, 2-deep ring
-    {256, 256, 32, 2, 4, 4},   // 8: 8 waves (2 per SIMD), 128x64 per wave, 4-deep ring
-    {256, 256, 64, 2, 4, 2},   // 9: 8 waves, 128x64 per wave, 2-deep ring
-    // two work-groups per CU (<= 80 KiB LDS, <= 256 registers per lane each)
-    {256, 128, 32, 2, 2, 3, 2},  // 10: 128x64 per wave, 3-deep ring
-    {128, 256, 32, 2, 2, 3, 2},  // 11: 64x128 per wave, 3-deep ring
-    {256, 128, 32, 2, 2, 2, 2},  // 12: 128x64 per wave, 2-deep ring
-    {128, 128, 64, 2, 2, 2, 2},  // 13: 64x64 per wave
-    // 8 waves, copies issued by the second wave of each SIMD only
-    {256, 256, 64, 2, 4, 2, 1, 4},  // 14
-    {256, 256, 32, 2, 4, 4, 1, 4},  // 15
+    {64, 64, 64, 2, 2, 2},     // 0: 32x32 per wave -- small and ragged problems, short K
+    {128, 128, 64, 2, 2, 2},   // 1: 64x64 per wave -- MFMA-bound products with 128-256 such tiles
+    {32, 128, 64, 1, 4, 2},    // 2: one 32-row tile -- thin M that the skinny kernel does not take
+    {256, 256, 32, 2, 4, 4},   // 3: 8 waves (2 per SIMD), 128x64 per wave, 4-deep ring -- grouped
+                               //    MFMA-bound launches; K = 0 on a ping-pong plan
+    {128, 128, 64, 2, 2, 2, 2},  // 4: 64x64 per wave, two work-groups per CU -- HBM-bound products
     // three or four work-groups per CU: small rings for short K, where the
-    // loads are latency-bound and only concurrency hides them
-    {128, 128, 32, 2, 2, 2, 4},  // 16: 32 KiB
-    {128, 128, 32, 2, 2, 3, 3},  // 17: 48 KiB
-    {64, 128, 64, 2, 2, 2, 3},   // 18: 32x64 per wave, 48 KiB
-    {128, 64, 64, 2, 2, 2, 4},   // 19: 64x32 per wave, 32 KiB
-    // 5-deep rings (160 KiB): three K steps between a stage's copies and
-    // their use -- a single wave per SIMD has nothing else to hide latency
-    {256, 256, 32, 2, 2, 5},     // 20: 4 waves, 128x128 per wave
-    {256, 256, 32, 2, 4, 5},     // 21: 8 waves, 128x64 per wave
-    // 8 waves, 4 of them copy: persistent work-groups whose copy waves
-    // prefetch while the other waves store (split mode)
-    {128, 128, 64, 2, 4, 2, 2, 4},  // 22: 64x32 per wave, 64 KiB
+    // loads are latency-bound and only concurrency hides them (grouped launches)
+    {128, 128, 32, 2, 2, 2, 4},  // 5: 32 KiB
+    {128, 128, 32, 2, 2, 3, 3},  // 6: 48 KiB
+    {128, 64, 64, 2, 2, 2, 4},   // 7: 64x32 per wave, 32 KiB
     // 8 waves in two groups that alternate MFMA and memory phases
     // (pingpong_gemm.hpp): 128x64 per wave, 64-deep K steps, three A and two
     // B LDS buffers (160 KiB); the second entry adds the epilogue
-    {256, 256, 64, 2, 4, 2, 1, 4, kPingPong},     // 23
-    {256, 256, 64, 2, 4, 2, 1, 4, kPingPongEpi},  // 24
+    {256, 256, 64, 2, 4, 2, 1, 4, kPingPong},     // 8
+    {256, 256, 64, 2, 4, 2, 1, 4, kPingPongEpi},  // 9
     // 4 waves walking runs of 128 x 128 tiles along a row panel of C, K <=
     // 128 (panel_gemm.hpp): A in registers, two B LDS buffers (64 KiB), two
     // work-groups per CU
-    {128, 128, 128, 2, 2, 2, 2, 0, kPanel},  // 25
-    // 64x64 tiles with deep rings for small, latency-bound products: with
-    // a K step's MFMAs far shorter than a copy's round trip, the time per
-    // step is the round trip divided by the steps in flight
-    {64, 64, 64, 2, 2, 4, 2},  // 26: 4-deep ring, 64 KiB
-    {64, 64, 32, 2, 2, 5, 3},  // 27: 5-deep ring of 32-deep steps, 40 KiB
+    {128, 128, 128, 2, 2, 2, 2, 0, kPanel},  // 10
+    // 64x64 tiles with a deep ring for small, latency-bound products with a
+    // long K: with a K step's MFMAs far shorter than a copy's round trip, the
+    // time per step is the round trip divided by the steps in flight
+    {64, 64, 64, 2, 2, 4, 2},  // 11: 4-deep ring, 64 KiB
 };
-constexpr int kPingPongTile = 23, kPingPongEpiTile = 24, kPanelTile = 25;
+constexpr int kSmallTile = 0, kMfmaMidTile = 1, kThinTile = 2, kWideTile = 3, kHbmTile = 4, kDeepSmallTile = 11;
+constexpr int kPingPongTile = 8, kPingPongEpiTile = 9, kPanelTile = 10;
 constexpr int kPanelKMax = kTiles[kPanelTile].bk;  // the panel kernel holds all of K at once
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -79,7 +60,7 @@ constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // groups, two HBM/MFMA-balanced 128x128 shapes, the large 8-wave tile, and
 // three shapes with three or four work-groups per CU for groups that stream
 // their B operands (more copies in flight per CU).
-constexpr int kGroupTiles[] = {0, 13, 1, 8, 17, 16, 19};
+constexpr int kGroupTiles[] = {kSmallTile, kHbmTile, kMfmaMidTile, kWideTile, 6, 5, 7};
 constexpr int kNumGroup = sizeof(kGroupTiles) / sizeof(kGroupTiles[0]);
 
 constexpr TileShape kGenericTiles[] = {
@@ -98,18 +79,6 @@ constexpr int lds_bytes_of(const TileShape& t) {
 // prefetched item counts the copy instructions of the stages after the first
 // one plus the item's store instructions, and that count must fit the 6-bit
 // vector-memory counter.
-// Whether the tile kernel can run in split mode for a given output element
-// size: dedicated copy waves, a C tile that fits the ring's LDS in one band,
-// and a band that divides evenly over the waves that store it.
-constexpr bool split_ok(const TileShape& t, int out_size) {
-  if (t.kind != kTileKernel) return false;
-  const int nw = t.wm * t.wn;
-  const int stores = nw - (t.dw ? t.dw : nw);
-  const int c_bytes = t.bm * t.bn * out_size;
-  return stores > 0 && t.bn * out_size / 16 >= 4 && c_bytes <= lds_bytes_of(t) &&
-         (c_bytes / 16) % (stores * 64) == 0;
-}
-
 constexpr bool persist_ok(const TileShape& t) {
   if (t.kind != kTileKernel) return false;
   const int copy_waves = t.dw ? t.dw : t.wm * t.wn;
@@ -129,12 +98,6 @@ struct SkinnyShape {
 constexpr SkinnyShape kSkinny[] = {
     {1, 1, 4, 3, 256},  // 0: M <= 16, 16 columns, 48 KiB (three work-groups per CU)
     {2, 2, 8, 4, 256},  // 1: M <= 32, 128 KiB
-    {1, 1, 2, 4, 256},  // 2: M <= 16, 16 columns, 2 waves, 64 KiB
-    {1, 1, 8, 4, 256},  // 3: M <= 16, 16 columns, 8 waves, 64 KiB
-    {1, 1, 4, 5, 256},  // 4: M <= 16, 16 columns, 80 KiB (two work-groups per CU)
-    {1, 1, 4, 4, 256},  // 5: M <= 16, 16 columns, 64 KiB
-    {2, 1, 4, 3, 256},  // 6: M <= 32, 16 columns, 72 KiB
-    {1, 2, 8, 4, 256},  // 7: M <= 16, 32 columns, 96 KiB
 };
 constexpr int kNumSkinny = sizeof(kSkinny) / sizeof(kSkinny[0]);
 constexpr int skinny_lds_of(const SkinnyShape& s) { return s.stages * (16 * s.nb + 16 * s.mb) * 2 * s.sk; }

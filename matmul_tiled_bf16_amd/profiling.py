@@ -12,6 +12,10 @@
     python -m matmul_tiled_bf16_amd.profiling stats OUT/trace [gemm|group|attention] > profiles/<kernel>_<workload>_stats.txt
     python -m matmul_tiled_bf16_amd.profiling traffic OUT <workload> > profiles/<workload>_traffic.txt
 
+    # counters of the intact kernel (four passes, each its own run; PASSES below):
+    rocprofv3 --pmc <PASSES[i]> --output-format csv -d OUT/pmc<i+1> -o run -- python bench.py ...
+    python -m matmul_tiled_bf16_amd.profiling counters OUT <kernel-name-part> > profiles/<kernel>_<workload>_counters.txt
+
 FETCH_SIZE / WRITE_SIZE are reported in KiB per dispatch; the copy kernel
 moves a known number of bytes, and the ratio of that number to what the
 counter reads for it scales the kernel's reading to bytes.  A traffic file
@@ -152,11 +156,110 @@ def read_traffic(workload: str):
     return float(kv["traffic_bytes"])
 
 
+# Counter passes for the utilisation summary: each fits one rocprofv3 pass
+# (at most 8 SQ, 4 TCC and 2 GRBM counters).
+PASSES = [
+    "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES "
+    "SQ_BUSY_CU_CYCLES SQ_WAVE_CYCLES SQ_WAVES GRBM_GUI_ACTIVE",
+    "SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_LDS_CMD_FIFO_FULL "
+    "SQ_LDS_ADDR_CONFLICT SQ_LDS_UNALIGNED_STALL GRBM_GUI_ACTIVE",
+    "TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE",
+    "SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_VMEM_RD "
+    "SQ_INSTS_VMEM_WR SQ_WAVES",
+]
+N_XCD = 8            # MI355X: GRBM_GUI_ACTIVE reads the sum over its 8 XCDs
+N_SIMD = 256 * 4     # 256 CUs x 4 SIMDs
+FLOP_PER_CU_CLK = 4096  # dense bf16/fp16 MFMA
+
+
+def _dispatches(path_dir: str, match):
+    """{dispatch: {counter: value, '_ns': duration, '_regs': (...)}} for matching kernels."""
+    out = defaultdict(dict)
+    for r in _csv(path_dir, "counter_collection.csv"):
+        if not match(r["Kernel_Name"]):
+            continue
+        d = out[r["Dispatch_Id"]]
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        d["_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        d["_name"] = r["Kernel_Name"]
+        d["_regs"] = (r.get("VGPR_Count"), r.get("Accum_VGPR_Count"), r.get("SGPR_Count"), r.get("Scratch_Size"),
+                      r.get("Workgroup_Size"), r.get("Grid_Size"))
+    return out
+
+
+def counters(out_dir: str, pattern: str) -> str:
+    """Utilisation summary of the kernels whose name contains `pattern`, from the
+    four PASSES runs under out_dir/pmc1 .. pmc4 (means over their dispatches)."""
+    passes = [_dispatches(os.path.join(out_dir, f"pmc{i + 1}"), lambda n: pattern in n) for i in range(len(PASSES))]
+    mean = lambda ds, key: sum(d[key] for d in ds.values()) / len(ds)
+    v = defaultdict(lambda: float("nan"))
+    for ds in passes:
+        for key in next(iter(ds.values())):
+            if not key.startswith("_") and key not in v:
+                v[key] = mean(ds, key)
+    p1 = passes[0]
+    any_d = next(iter(p1.values()))
+    ns = sum(mean(ds, "_ns") for ds in passes) / len(passes)
+    cyc = v["GRBM_GUI_ACTIVE"] / N_XCD
+    flops = 512.0 * (v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + v.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0))
+    wave_cyc = 4.0 * v["SQ_WAVE_CYCLES"]  # quad-cycles
+    hits, miss = v["TCC_HIT_sum"], v["TCC_MISS_sum"]
+    vg, ag, sg, scratch, wg, grid = any_d["_regs"]
+    fam = next((f for f, (pats, _) in FAMILIES.items() if any(q in any_d["_name"] for q in pats)), "gemm")
+    lines = [
+        f"# rocprofv3 counters of {_short(any_d['_name'])}",
+        f"source_hash = {source_hash(fam)}  ({fam} sources)",
+        f"dispatches per pass = {[len(ds) for ds in passes]}",
+        f"duration_us (counter runs) = {ns / 1e3:.2f}",
+        f"registers: vgpr = {vg}, agpr = {ag}, sgpr = {sg}, scratch_bytes = {scratch}, "
+        f"workgroup = {wg}, grid_threads = {grid}",
+        "",
+        "## clock and matrix cores",
+        f"GRBM_GUI_ACTIVE per XCD = {cyc:.0f} cycles  -> shader clock {cyc / ns:.3f} GHz during the kernel",
+        f"SQ_INSTS_MFMA = {v['SQ_INSTS_MFMA']:.0f}",
+        f"MFMA flops (MOPS x 512) = {flops:.4g}",
+        f"SQ_VALU_MFMA_BUSY_CYCLES = {v['SQ_VALU_MFMA_BUSY_CYCLES']:.0f}",
+        f"MFMA busy = busy / (cycles x {N_SIMD} SIMDs) = {100 * v['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * N_SIMD):.1f} %",
+        f"MFMA flops / (cycles x 256 CUs x {FLOP_PER_CU_CLK}) = {100 * flops / (cyc * 256 * FLOP_PER_CU_CLK):.1f} %"
+        f"  (of the peak at the measured clock)",
+        f"MFMA flops / duration = {flops / ns / 1e3:.1f} TFLOP/s",
+        f"CU busy = SQ_BUSY_CU_CYCLES / (cycles x 256) = {100 * v['SQ_BUSY_CU_CYCLES'] / (cyc * 256):.1f} %",
+        "",
+        "## LDS",
+        f"SQ_INSTS_LDS = {v['SQ_INSTS_LDS']:.0f}",
+        f"SQ_LDS_BANK_CONFLICT = {v['SQ_LDS_BANK_CONFLICT']:.0f} cycles"
+        f"  ({100 * v['SQ_LDS_BANK_CONFLICT'] / v['SQ_LDS_IDX_ACTIVE']:.2f} % of SQ_LDS_IDX_ACTIVE)",
+        f"SQ_LDS_ADDR_CONFLICT = {v['SQ_LDS_ADDR_CONFLICT']:.0f}, SQ_LDS_UNALIGNED_STALL = {v['SQ_LDS_UNALIGNED_STALL']:.0f}",
+        f"SQ_LDS_IDX_ACTIVE = {v['SQ_LDS_IDX_ACTIVE']:.0f}  ({100 * v['SQ_LDS_IDX_ACTIVE'] / (cyc * 256):.1f} % of CU cycles)",
+        f"SQ_LDS_CMD_FIFO_FULL = {v['SQ_LDS_CMD_FIFO_FULL']:.0f}  ({100 * v['SQ_LDS_CMD_FIFO_FULL'] / (cyc * 256):.1f} % of CU cycles)",
+        f"SQ_WAIT_INST_LDS = {v['SQ_WAIT_INST_LDS']:.0f} quad-cycles ({100 * 4 * v['SQ_WAIT_INST_LDS'] / wave_cyc:.1f} % of wave time)",
+        "",
+        "## L2",
+        f"TCC_HIT_sum = {hits:.0f}, TCC_MISS_sum = {miss:.0f}, hit rate = {100 * hits / (hits + miss):.1f} %",
+        "",
+        "## waves (fractions of SQ_WAVE_CYCLES, quad-cycles)",
+        f"SQ_WAVES = {v['SQ_WAVES']:.0f}",
+        f"waiting on anything (SQ_WAIT_ANY) = {100 * 4 * v['SQ_WAIT_ANY'] / wave_cyc:.1f} %",
+        f"waiting for an issue slot (SQ_WAIT_INST_ANY) = {100 * 4 * v['SQ_WAIT_INST_ANY'] / wave_cyc:.1f} %",
+        f"issuing (SQ_ACTIVE_INST_ANY) = {100 * 4 * v['SQ_ACTIVE_INST_ANY'] / wave_cyc:.1f} %",
+        f"instructions per wave: VALU (incl. MFMA) {v['SQ_INSTS_VALU'] / v['SQ_WAVES']:.0f}, "
+        f"MFMA {v['SQ_INSTS_MFMA'] / v['SQ_WAVES']:.0f}, SALU {v['SQ_INSTS_SALU'] / v['SQ_WAVES']:.0f}, "
+        f"LDS {v['SQ_INSTS_LDS'] / v['SQ_WAVES']:.0f}, VMEM read {v['SQ_INSTS_VMEM_RD'] / v['SQ_WAVES']:.0f}, "
+        f"VMEM write {v['SQ_INSTS_VMEM_WR'] / v['SQ_WAVES']:.0f}",
+    ]
+    return "\n".join(lines)
+
+
 def main(argv):
     if argv[0] == "stats":
         print(stats(argv[1], argv[2] if len(argv) > 2 else "gemm"))
     elif argv[0] == "traffic":
         print(traffic(argv[1], argv[2]))
+    elif argv[0] == "counters":
+        print(counters(argv[1], argv[2]))
+    elif argv[0] == "passes":
+        for ps in PASSES:
+            print(ps)
     elif argv[0] == "hash":
         print(source_hash(argv[1] if len(argv) > 1 else "gemm"))
     else:

@@ -153,7 +153,7 @@ def test_plan_choices_for_the_workloads():
         for tb in (0, 1):
             p = tg.plan(1000, 1000, 1000, trans_a=ta, trans_b=tb)
             assert p.variant == tg.VARIANT_TILE and p.flags & tg.FLAG_VEC16 and not p.flags & tg.FLAG_EVEN_K
-            assert (p.tile, p.bm, p.bn, p.stages) == (26, 64, 64, 4)  # small, long K: the 4-deep 64x64 ring
+            assert (p.tile, p.bm, p.bn, p.stages) == (11, 64, 64, 4)  # small, long K: the 4-deep 64x64 ring
             assert p.tiles_m * p.tiles_n >= 64
     # skinny M = 16, B stored N x K
     import torch
@@ -178,10 +178,10 @@ def test_plan_choices_for_the_workloads():
     # tiles keep the 128 x 128 tile kernel
     assert tg.plan(2048, 2048, 128, trans_b=True, batch=128).tile == tg.TILE_PANEL
     assert tg.plan(2048, 2048, 64, batch=128, out_dtype=torch.bfloat16).tile == tg.TILE_PANEL
-    assert tg.plan(2048, 2048, 128, trans_a=True, trans_b=True, batch=128).tile == 13
-    assert tg.plan(2048, 2048, 136, trans_b=True, batch=128).tile == 13
-    assert tg.plan(2048, 2048, 128, trans_b=True).tile == 13
-    assert tg.plan(2048, 128, 2048, batch=128).tile == 13
+    assert tg.plan(2048, 2048, 128, trans_a=True, trans_b=True, batch=128).tile == 4
+    assert tg.plan(2048, 2048, 136, trans_b=True, batch=128).tile == 4
+    assert tg.plan(2048, 2048, 128, trans_b=True).tile == 4
+    assert tg.plan(2048, 128, 2048, batch=128).tile == 4
     with pytest.raises(tg.TgError):
         tg.plan(64, 64, 64, batch=0)
     p = tg.plan(8192, 8192, 8192, out_dtype=torch.bfloat16)
@@ -191,7 +191,7 @@ def test_plan_choices_for_the_workloads():
     assert tg.plan(1024, 1024, 4096, batch=16).tile == tg.TILE_PINGPONG                # 16 x 16 items
     assert tg.plan(2048, 2048, 8192, out_dtype=torch.bfloat16).tile == 1                # 64 items: 128 x 128
     assert tg.plan(1536, 1536, 8192, out_dtype=torch.bfloat16).tile == 1                # 144 128 x 128 items
-    assert tg.plan(1024, 2048, 8192, out_dtype=torch.bfloat16).tile == 26               # 128: the 64 x 64 ring
+    assert tg.plan(1024, 2048, 8192, out_dtype=torch.bfloat16).tile == 11               # 128: the 64 x 64 ring
     assert p.flags & tg.FLAG_PERSIST and p.flags & tg.FLAG_PREFETCH  # MFMA-bound: prefetch during stores
     assert p.workspace_bytes == 0
 
@@ -406,3 +406,46 @@ def test_splitk_host_side():
     # an empty product enqueues nothing
     e = tg.plan(0, 16, 64)
     assert L.gemm_splitk_run(ctypes.byref(e), 2, None, 0, None, None, None, None) == tg.TG_OK
+
+
+# ---- the Python binding's operand checks (CPU tensors: the structural checks
+# run before the device check, so each bad layout is refused by its own message
+# and nothing reaches the library)
+
+def _bf(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("make,msg", [
+    (lambda: _bf(4, 8, 2), "must be a 2-D"),                              # 3-D where a matrix is expected
+    (lambda: _bf(8).expand(4, 8), "rows overlap"),                        # row stride 0
+    (lambda: _bf(8, 4).t(), "contiguous last dimension"),                 # transposed view
+    (lambda: _bf(4, 16)[:, ::2], "contiguous last dimension"),            # strided columns
+    (lambda: _bf(4, 8), "GPU tensor"),                                    # well-formed, but on the host
+])
+def test_binding_rejects_bad_operand_layouts(make, msg):
+    with pytest.raises(ValueError, match=msg):
+        tg.gemm(make(), _bf(8, 8))
+
+
+def test_binding_rejects_bad_outputs_before_launch():
+    import torch
+    A, B = _bf(4, 8), _bf(8, 6)
+    with pytest.raises(ValueError, match="wrong shape or dtype"):
+        tg._check_out(_bf(4, 6), (4, 6), torch.float32)             # bf16 out, fp32 requested
+    with pytest.raises(ValueError, match="contiguous last dimension"):
+        tg._check_out(torch.zeros(6, 4).t(), (4, 6), torch.float32)  # transposed out
+    with pytest.raises(ValueError, match="rows overlap"):
+        tg._check_out(torch.zeros(6).expand(4, 6), (4, 6), torch.float32)
+    with pytest.raises(ValueError, match="batch overlap"):
+        tg._check_out(torch.zeros(4, 6).expand(3, 4, 6), (3, 4, 6), torch.float32, (3,))
+    with pytest.raises(ValueError, match="must be a 3-D"):
+        tg.bmm(A, B)
+    with pytest.raises(ValueError, match="must be a 2-D"):
+        tg.gemm_splitk(_bf(2, 4, 8), B)
+    with pytest.raises(ValueError, match="must be a 2-D"):
+        tg.gemm_group([_bf(2, 4, 8)], [B])
+    # a well-formed host output still stops at the device check
+    with pytest.raises(ValueError, match="GPU tensor"):
+        tg._check_out(torch.zeros(3, 4, 6), (3, 4, 6), torch.float32, (3,))

@@ -137,7 +137,8 @@ def test_every_tile_gives_the_same_answer():
 
 
 def test_skinny_variants_and_tails():
-    cases = [(t, 16) for t in range(tg.variant_tiles(tg.VARIANT_SKINNY)) if t != 1] + [(1, 32), (1, 17), (2, 5)]
+    assert tg.variant_tiles(tg.VARIANT_SKINNY) == 2
+    cases = [(0, 16), (0, 5), (1, 32), (1, 17)]
     for tile, m in cases:
         # K of only a few stages makes most ring refills read out of range
         # (they return zeros at once): the refill must not overtake another
@@ -184,9 +185,7 @@ def test_batched_broadcast_and_strides():
 @pytest.mark.parametrize("ta,tb,out_dtype", [(0, 0, "fp32"), (1, 1, "fp32"), (0, 1, "fp32"), (0, 1, "bf16")])
 def test_persistent_launch_matches_one_workgroup_per_tile(ta, tb, out_dtype):
     """Persistent work-groups (each loops over tiles; with PREFETCH the next
-    tile's first copies are issued before this tile's stores -- by every wave,
-    or, for kernels with dedicated copy waves, by the copy waves while the
-    other waves store the tile through LDS) compute exactly what one
+    tile's first copies are issued before this tile's stores) compute exactly what one
     work-group per tile computes -- the K walk and the summation order are the
     same -- on ragged batched shapes with enough tiles that the launcher does
     loop, with a masked K tail and with a K of several ring lengths."""
@@ -205,8 +204,8 @@ def test_persistent_launch_matches_one_workgroup_per_tile(ta, tb, out_dtype):
         ref = oracle.gemm(A, B, m=m, n=n, k=k, trans_a=ta, trans_b=tb, batch=batch, stride_a=ar * ac,
                           stride_b=br * bc, idx=idx)
         t = tol_fp32(k, oracle.max_abs(A), oracle.max_abs(B))
-        # 0, 1, 8, 13: every wave copies; 15, 22: dedicated copy waves (22: split mode)
-        for tile in (0, 1, 8, 13, 15, 22):
+        # every tile-kernel entry the planner or the grouped launch uses for these shapes
+        for tile in (0, 1, 3, 4, 11):
             outs = []
             both = tg.FLAG_PERSIST | tg.FLAG_PREFETCH
             for flags in (both, tg.FLAG_PERSIST, 0):

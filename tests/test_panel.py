@@ -142,7 +142,7 @@ def test_batches_that_share_an_operand(case):
         B = synth.draw(rng, (n, k), "int", -4, 4)
         sA, sB = m * k, 0
     else:
-        m, n, k, tb, tile = 520, 128, 1000, 0, 13
+        m, n, k, tb, tile = 520, 128, 1000, 0, 4  # the 128 x 128 tile kernel
         A = synth.draw(rng, (m, k) if case == "one_column_shared_A" else (batch, m, k), "int", -4, 4)
         B = synth.draw(rng, (batch, k, n), "int", -4, 4)
         sA, sB = (0 if case == "one_column_shared_A" else m * k), k * n
