@@ -26,8 +26,10 @@
  * operand for every batch; C strides must not make batches overlap).
  *
  * Ownership: every pointer is caller-owned device memory (A, B, C) or
- * caller-owned host memory (the plan).  The library allocates nothing, keeps
- * no global mutable state and is safe to call from several host threads.
+ * caller-owned host memory (the plan).  The library allocates nothing and is
+ * safe to call from several host threads.  Its only process state is a
+ * per-device cache of the compute-unit count and, for
+ * gemm_splitk_run_noalloc, one fixed scratch array per device (see there).
  * C must not alias A or B.
  *
  * Errors are returned as tg_status codes; the library never aborts or throws.
@@ -50,7 +52,8 @@ typedef enum {
   TG_OK = 0,
   TG_ERR_INVALID = 1,     /* bad argument: sizes, leading dims, flags, null pointers, plan */
   TG_ERR_UNSUPPORTED = 2, /* well-formed but not provided: dtype pair, forced variant/tile */
-  TG_ERR_HIP = 3          /* the HIP runtime rejected the launch */
+  TG_ERR_HIP = 3,         /* the HIP runtime rejected the launch */
+  TG_ERR_TOO_LARGE = 4    /* the problem needs more scratch than the library's fixed array holds */
 } tg_status;
 
 /* Kernel families a plan can select. */
@@ -253,6 +256,31 @@ int32_t tg_group_tiles(void);
 #define TG_SPLITK_MAX 32
 tg_status gemm_splitk_run(const gemm_plan_t* plan, int32_t splits, void* workspace, uint64_t workspace_bytes,
                           const void* A, const void* B, void* C, hipStream_t stream);
+
+/*
+ * gemm_splitk_run_noalloc -- gemm_splitk_run without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The partial
+ * products go to a fixed array of TG_SPLITK_SCRATCH_BYTES in device memory
+ * that the library holds once per GPU until the process ends; its device
+ * address is looked up on the first call on each device (with that device
+ * current).  Nothing is allocated and no allocating routine is called.
+ *   Same arguments, results and errors as gemm_splitk_run (the parts, the
+ *   reduction and the order of additions are the same, so the results are
+ *   bit-identical), plus TG_ERR_TOO_LARGE when
+ *   tg_splitk_workspace_bytes(plan, splits) > TG_SPLITK_SCRATCH_BYTES
+ *   (checked before any device call), and TG_ERR_HIP if the device or the
+ *   array's address cannot be obtained.
+ *   Every call on one GPU uses that GPU's one array, and the array keeps the
+ *   last call's partial products: calls that may overlap on one GPU (several
+ *   streams, or several host threads, at once) race and give wrong results;
+ *   serialise them (one stream, or events between them).  The reduction reads
+ *   only what the parts of the same call wrote, so nothing has to start at
+ *   zero.
+ */
+#define TG_SPLITK_SCRATCH_BYTES (64ull << 20)
+tg_status gemm_splitk_run_noalloc(const gemm_plan_t* plan, int32_t splits, const void* A, const void* B, void* C,
+                                  hipStream_t stream);
 
 /* Workspace bytes gemm_splitk_run needs for `plan` and `splits`
  * (parts * m * ldw * 4); 0 for an invalid plan or split count, or K = 0. */

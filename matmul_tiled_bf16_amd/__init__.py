@@ -22,11 +22,12 @@ LIB_PATH = os.path.join(HERE, "libtgemm.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "tgemm.h")
 
 TG_BF16, TG_FP16, TG_FP32 = 0, 1, 2
-TG_OK, TG_ERR_INVALID, TG_ERR_UNSUPPORTED, TG_ERR_HIP = 0, 1, 2, 3
+TG_OK, TG_ERR_INVALID, TG_ERR_UNSUPPORTED, TG_ERR_HIP, TG_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 VARIANT_GENERIC, VARIANT_TILE, VARIANT_SKINNY = 0, 1, 2
 TILE_PINGPONG, TILE_PINGPONG_EPI = 8, 9  # TG_TILE_PINGPONG, TG_TILE_PINGPONG_EPI
 TILE_PANEL = 10  # TG_TILE_PANEL
 SPLITK_MAX = 32  # TG_SPLITK_MAX
+SPLITK_SCRATCH_BYTES = 64 << 20  # TG_SPLITK_SCRATCH_BYTES
 FLAG_EVEN_K, FLAG_VEC16, FLAG_ROTATE_K, FLAG_PERSIST, FLAG_PREFETCH, FLAG_STREAM_C = 0x1, 0x2, 0x4, 0x8, 0x10, 0x20
 
 
@@ -114,6 +115,8 @@ def lib() -> ctypes.CDLL:
         L.tg_group_tiles.argtypes = []
         L.gemm_splitk_run.restype = ctypes.c_int
         L.gemm_splitk_run.argtypes = [ctypes.POINTER(GemmPlan), i32, p, ctypes.c_uint64, p, p, p, p]
+        L.gemm_splitk_run_noalloc.restype = ctypes.c_int
+        L.gemm_splitk_run_noalloc.argtypes = [ctypes.POINTER(GemmPlan), i32, p, p, p, p]
         L.tg_splitk_workspace_bytes.restype = ctypes.c_uint64
         L.tg_splitk_workspace_bytes.argtypes = [ctypes.POINTER(GemmPlan), i32]
         L.tg_splitk_choose.restype = i32
@@ -306,6 +309,15 @@ def gemm_splitk_run(p: GemmPlan, splits: int, workspace, workspace_bytes: int, A
                                _ptr(C), _stream_handle(stream))
     if st != TG_OK:
         raise TgError(st, "gemm_splitk_run")
+
+
+def gemm_splitk_run_noalloc(p: GemmPlan, splits: int, A, B, C, stream=None) -> None:
+    """gemm_splitk_run_noalloc(): split-K through the library's fixed per-device scratch
+    array (no workspace, no allocation); calls that overlap on one GPU race."""
+    st = lib().gemm_splitk_run_noalloc(ctypes.byref(p), int(splits), _ptr(A), _ptr(B), _ptr(C),
+                                       _stream_handle(stream))
+    if st != TG_OK:
+        raise TgError(st, "gemm_splitk_run_noalloc")
 
 
 def gemm_splitk(A, B, *, trans_a: bool = False, trans_b: bool = False, out_dtype=None, out=None,

@@ -15,9 +15,37 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/tgemm.h"
 
+// Partial products of gemm_splitk_run_noalloc: a fixed array in device
+// memory, one copy per GPU the library runs on, held until the process ends.
+// Host code never passes this name to a kernel (on the host it only stands in
+// for the symbol); it asks the runtime for each device's address once and
+// uses that.
+static __device__ __align__(256) float scratch[TG_SPLITK_SCRATCH_BYTES / sizeof(float)];
+
 namespace {
+
+// Device address of `scratch` on each device, filled on the first
+// gemm_splitk_run_noalloc call on that device (racing fills store the same
+// value).
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+tg_status scratch_of_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return TG_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return TG_ERR_UNSUPPORTED;
+  void* ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return TG_ERR_HIP;
+    g_scratch_addr[dev].store(ptr, std::memory_order_release);
+  }
+  *out = static_cast<float*>(ptr);
+  return TG_OK;
+}
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -100,8 +128,12 @@ int32_t tg_splitk_choose(const gemm_plan_t* plan) {
   return (int32_t)(s < 1 ? 1 : s);
 }
 
-tg_status gemm_splitk_run(const gemm_plan_t* plan, int32_t splits, void* workspace, uint64_t workspace_bytes,
-                          const void* A, const void* B, void* C, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by both entry points (everything but the workspace).
+tg_status splitk_check(const gemm_plan_t* plan, int32_t splits, const void* A, const void* B, const void* C) {
   if (!plan || plan->abi_version != TG_ABI_VERSION) return TG_ERR_INVALID;
   if (splits < 1 || splits > TG_SPLITK_MAX) return TG_ERR_INVALID;
   const gemm_plan_t& p = *plan;
@@ -109,12 +141,15 @@ tg_status gemm_splitk_run(const gemm_plan_t* plan, int32_t splits, void* workspa
   if (p.m == 0 || p.n == 0) return TG_OK;
   if (!C) return TG_ERR_INVALID;
   if (p.k > 0 && (!A || !B)) return TG_ERR_INVALID;
-  const Parts g = parts_of(p, splits);
-  const uint64_t need = tg_splitk_workspace_bytes(plan, splits);
-  if (p.k > 0 && (need == 0 || !workspace || workspace_bytes < need || (uintptr_t)workspace % 16 != 0))
-    return TG_ERR_INVALID;
+  if (p.k > 0 && tg_splitk_workspace_bytes(plan, splits) == 0) return TG_ERR_INVALID;
+  return TG_OK;
+}
 
-  float* W = static_cast<float*>(workspace);
+// Enqueue the parts into the fp32 workspace W (large enough, 16-byte
+// aligned, checked by the caller) and the reduction into C.
+tg_status splitk_enqueue(const gemm_plan_t& p, int32_t splits, float* W, const void* A, const void* B, void* C,
+                         hipStream_t stream) {
+  const Parts g = parts_of(p, splits);
   const int64_t slice = p.m * g.ldw;  // floats per part
   const char* a = static_cast<const char*>(A);
   const char* b = static_cast<const char*>(B);
@@ -158,6 +193,30 @@ tg_status gemm_splitk_run(const gemm_plan_t* plan, int32_t splits, void* workspa
     hipLaunchKernelGGL(splitk_reduce_kernel<_Float16>, dim3(blocks), dim3(256), 0, stream, W, slice, parts, p.m,
                        p.n, g.ldw, static_cast<_Float16*>(C), p.ldc);
   return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+tg_status gemm_splitk_run(const gemm_plan_t* plan, int32_t splits, void* workspace, uint64_t workspace_bytes,
+                          const void* A, const void* B, void* C, hipStream_t stream) {
+  const tg_status st = splitk_check(plan, splits, A, B, C);
+  if (st != TG_OK || plan->m == 0 || plan->n == 0) return st;
+  const uint64_t need = tg_splitk_workspace_bytes(plan, splits);
+  if (plan->k > 0 && (!workspace || workspace_bytes < need || (uintptr_t)workspace % 16 != 0)) return TG_ERR_INVALID;
+  return splitk_enqueue(*plan, splits, static_cast<float*>(workspace), A, B, C, stream);
+}
+
+tg_status gemm_splitk_run_noalloc(const gemm_plan_t* plan, int32_t splits, const void* A, const void* B, void* C,
+                                  hipStream_t stream) {
+  const tg_status st = splitk_check(plan, splits, A, B, C);
+  if (st != TG_OK || plan->m == 0 || plan->n == 0) return st;
+  if (tg_splitk_workspace_bytes(plan, splits) > TG_SPLITK_SCRATCH_BYTES) return TG_ERR_TOO_LARGE;
+  float* W = nullptr;
+  const tg_status sw = scratch_of_current_device(&W);
+  if (sw != TG_OK) return sw;
+  return splitk_enqueue(*plan, splits, W, A, B, C, stream);
 }
 
 }  // extern "C"

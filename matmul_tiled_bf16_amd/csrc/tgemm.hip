@@ -194,6 +194,7 @@ const char* tg_status_str(tg_status s) {
     case TG_ERR_INVALID: return "invalid argument";
     case TG_ERR_UNSUPPORTED: return "unsupported";
     case TG_ERR_HIP: return "HIP launch error";
+    case TG_ERR_TOO_LARGE: return "problem exceeds the fixed scratch array";
   }
   return "unknown status";
 }

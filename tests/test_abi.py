@@ -353,6 +353,8 @@ def test_python_constants_match_the_header():
     assert int(defs["TG_TILE_PINGPONG_EPI"], 0) == tg.TILE_PINGPONG_EPI
     assert int(defs["TG_TILE_PANEL"], 0) == tg.TILE_PANEL
     assert int(defs["TG_SPLITK_MAX"], 0) == tg.SPLITK_MAX
+    m = re.search(r"#define\s+TG_SPLITK_SCRATCH_BYTES\s+\((\d+)ull << (\d+)\)", text)
+    assert int(m.group(1)) << int(m.group(2)) == tg.SPLITK_SCRATCH_BYTES
     for name in ("EVEN_K", "VEC16", "ROTATE_K", "PERSIST", "PREFETCH", "STREAM_C"):
         assert int(defs["TG_FLAG_" + name], 0) == getattr(tg, "FLAG_" + name)
 
@@ -406,6 +408,15 @@ def test_splitk_host_side():
     # an empty product enqueues nothing
     e = tg.plan(0, 16, 64)
     assert L.gemm_splitk_run(ctypes.byref(e), 2, None, 0, None, None, None, None) == tg.TG_OK
+    # the no-allocation variant: the same argument checks, and sizes beyond its
+    # fixed array refused before any device call
+    for pl, s, w, nb, a, b, c in calls:
+        if w is ws and nb == need:
+            assert L.gemm_splitk_run_noalloc(ctypes.byref(pl), s, a, b, c, None) == tg.TG_ERR_INVALID
+    big = tg.plan(1024, 1032, 65536)
+    assert tg.splitk_workspace_bytes(big, 16) > tg.SPLITK_SCRATCH_BYTES
+    assert L.gemm_splitk_run_noalloc(ctypes.byref(big), 16, A, A, A, None) == tg.TG_ERR_TOO_LARGE
+    assert L.gemm_splitk_run_noalloc(ctypes.byref(e), 2, None, None, None, None) == tg.TG_OK
 
 
 # ---- the Python binding's operand checks (CPU tensors: the structural checks
