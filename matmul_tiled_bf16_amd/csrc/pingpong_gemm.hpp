@@ -278,17 +278,19 @@ __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(GemmArgs args) {
   const int64_t total = (int64_t)args.tiles_m * args.tiles_n * args.batch;
   if ((int64_t)blockIdx.x >= total || K <= 0) return;  // (the launcher never sends K = 0 here)
   // This work-group's items are blockIdx.x, blockIdx.x + gridDim.x, ...; their
-  // K steps form one stream of nsteps steps.
-  const int64_t nk = (K + BK - 1) / BK;
-  const int64_t items = (total - 1 - (int64_t)blockIdx.x) / gridDim.x + 1;
-  const int64_t nsteps = items * nk;
+  // K steps form one stream of nsteps steps (the launcher keeps the launch's
+  // item count times nk below 2^31, so 32-bit counters do).
+  const int32_t nk = (int32_t)((K + BK - 1) / BK);
+  const int32_t items = (int32_t)((total - 1 - (int64_t)blockIdx.x) / gridDim.x + 1);
+  const int32_t nsteps = items * nk;
+  const bool k_ragged = K % BK != 0;  // the last step of each item is masked
 
   struct Item {
     int64_t b, m0, n0;
   };
   // item t of this work-group: work_coords' XCD-aware order in 32-bit
   // arithmetic (the launcher keeps total below 2^31)
-  auto item_of = [&](int64_t t) {
+  auto item_of = [&](int32_t t) {
     const uint32_t tot = (uint32_t)total, tm = (uint32_t)args.tiles_m, tn = (uint32_t)args.tiles_n;
     const uint32_t w0 = blockIdx.x + (uint32_t)t * gridDim.x;
     const uint32_t per = tot >> 3, rem = tot & 7, x = w0 & 7, local = w0 >> 3;
@@ -304,48 +306,55 @@ __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(GemmArgs args) {
   };
 
   // Copy cursor of one operand: the next step it copies, as (item, step in
-  // item), with that item's panel base and remaining bytes.
+  // item), with the source of that step and the bytes from there to the end
+  // of the matrix.  Advancing within an item is two 64-bit adds; only a new
+  // item recomputes its panel origin.
   struct Cursor {
-    int64_t t, k;
-    const char* base;
-    int64_t left0;
-  };
-  auto a_seek = [&](Cursor& c) {
-    const Item it = item_of(c.t);
-    c.base = (const char*)(args.A + it.b * args.sA + (A_KC ? it.m0 * lda : it.m0));
-    c.left0 = A_KC ? ((M - 1 - it.m0) * lda + K) * 2 : ((K - 1) * lda + (M - it.m0)) * 2;
-  };
-  auto b_seek = [&](Cursor& c) {
-    const Item it = item_of(c.t);
-    c.base = (const char*)(args.B + it.b * args.sB + (B_KC ? it.n0 * ldb : it.n0));
-    c.left0 = B_KC ? ((N - 1 - it.n0) * ldb + K) * 2 : ((K - 1) * ldb + (N - it.n0)) * 2;
+    int32_t t, k;
+    const char* ptr;
+    int64_t left;
   };
   const int64_t a_step = A_KC ? (int64_t)BK * 2 : (int64_t)BK * lda * 2;
   const int64_t b_step = B_KC ? (int64_t)BK * 2 : (int64_t)BK * ldb * 2;
+  auto a_seek = [&](Cursor& c) {
+    const Item it = item_of(c.t);
+    const int64_t o = (int64_t)c.k * a_step;
+    c.ptr = (const char*)(args.A + it.b * args.sA + (A_KC ? it.m0 * lda : it.m0)) + o;
+    c.left = (A_KC ? ((M - 1 - it.m0) * lda + K) * 2 : ((K - 1) * lda + (M - it.m0)) * 2) - o;
+  };
+  auto b_seek = [&](Cursor& c) {
+    const Item it = item_of(c.t);
+    const int64_t o = (int64_t)c.k * b_step;
+    c.ptr = (const char*)(args.B + it.b * args.sB + (B_KC ? it.n0 * ldb : it.n0)) + o;
+    c.left = (B_KC ? ((N - 1 - it.n0) * ldb + K) * 2 : ((K - 1) * ldb + (N - it.n0)) * 2) - o;
+  };
   OA oa;
   OB ob;
   oa.init(sw, lane, lda);
   ob.init(sw, lane, ldb);
-  // copy the cursor's step into buffer `buf`, then advance the cursor
+  // copy the cursor's step into buffer `buf`, then advance the cursor (the
+  // last step of an item is masked at K when K is not a multiple of BK)
   auto copy_a = [&](Cursor& c, uint32_t buf) {
-    const int64_t k_left = K - c.k * BK, off = c.k * a_step;
     const uint32_t dst = lds0 + buf * A_BYTES;
-    if (k_left >= BK)
-      oa.template issue<false>((const uint16_t*)(c.base + off), c.left0 - off, lda, dst, sw, lane, k_left);
+    if (k_ragged && c.k == nk - 1)
+      oa.template issue<true>((const uint16_t*)c.ptr, c.left, lda, dst, sw, lane, K % BK);
     else
-      oa.template issue<true>((const uint16_t*)(c.base + off), c.left0 - off, lda, dst, sw, lane, k_left);
+      oa.template issue<false>((const uint16_t*)c.ptr, c.left, lda, dst, sw, lane, BK);
+    c.ptr += a_step;
+    c.left -= a_step;
     if (++c.k == nk) {
       c.k = 0;
       if (++c.t < items) a_seek(c);
     }
   };
   auto copy_b = [&](Cursor& c, uint32_t buf) {
-    const int64_t k_left = K - c.k * BK, off = c.k * b_step;
     const uint32_t dst = lds0 + B_BASE + buf * B_BYTES;
-    if (k_left >= BK)
-      ob.template issue<false>((const uint16_t*)(c.base + off), c.left0 - off, ldb, dst, sw, lane, k_left);
+    if (k_ragged && c.k == nk - 1)
+      ob.template issue<true>((const uint16_t*)c.ptr, c.left, ldb, dst, sw, lane, K % BK);
     else
-      ob.template issue<true>((const uint16_t*)(c.base + off), c.left0 - off, ldb, dst, sw, lane, k_left);
+      ob.template issue<false>((const uint16_t*)c.ptr, c.left, ldb, dst, sw, lane, BK);
+    c.ptr += b_step;
+    c.left -= b_step;
     if (++c.k == nk) {
       c.k = 0;
       if (++c.t < items) b_seek(c);
@@ -419,7 +428,7 @@ __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(GemmArgs args) {
   // is stored after the loop, with the epilogue and the element-wise path
   // for any N.
   const bool persistent = !EPI && (int64_t)gridDim.x < total;
-  auto store_counted = [&](int64_t t) {
+  auto store_counted = [&](int32_t t) {
     const Item it = item_of(t);
     char* Cb = (char*)args.C + it.b * args.sC * (int64_t)sizeof(Out);
     const int64_t r0 = it.m0 + wm0, c0 = it.n0 + wn0;
@@ -428,7 +437,7 @@ __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(GemmArgs args) {
                              in ? ((M - 1 - r0) * ldc + (N - c0)) * (int64_t)sizeof(Out) : 0, ldc, in ? N - c0 : 0,
                              lane, acc);
   };
-  auto store_final = [&](int64_t t) {
+  auto store_final = [&](int32_t t) {
     const Item it = item_of(t);
     char* Cb = (char*)args.C + it.b * args.sC * (int64_t)sizeof(Out);
     const int64_t r0 = it.m0 + wm0, c0 = it.n0 + wn0;
@@ -475,62 +484,75 @@ __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(GemmArgs args) {
   barrier();
   if (grp == 1) barrier();  // group 1 runs one phase behind
 
-  int64_t kk = 0, t = 0;  // step within the item, item
-  uint32_t abuf = 0, bbuf = 0;  // buffers of step g
-  for (int64_t g = 0; g < nsteps; ++g) {
-    fra.pin();
-    frb.pin();
-    oa.pin();
-    ob.pin();
-    // memory phase: this group's copies, the previous item's stores (after
-    // the copies, so that the waits may leave them in flight), then the
-    // fragments of step g
-    const bool stored = !EPI && kk == 0 && g > 0;
-    bool copied = false;
-    if (grp == 0) {
-      if (g + 1 < nsteps) {
-        copy_b(cur, bbuf ^ 1u);
-        copied = true;
-      }
-    } else if (g + 2 < nsteps) {
-      copy_a(cur, abuf == 0 ? 2u : abuf - 1);
-      copied = true;
-    }
-    if constexpr (!EPI) {
-      if (stored) store_counted(t - 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    mem(abuf, bbuf);
-    if (grp == 1) {
-      // A(g + 1) has landed; A(g + 2) and the stores may still be in flight
-      if (copied) {
-        if (stored) wait_vmcnt<PA + ST, true>();
-        else wait_vmcnt<PA, true>();
+  // The K-step loop, compiled once per group (the group is uniform over a
+  // wave), so that each wave's loop carries only its own copies and waits.
+  auto run = [&](auto group) {
+    constexpr int G = decltype(group)::value;
+    int32_t kk = 0, t = 0;        // step within the item, item
+    uint32_t abuf = 0, bbuf = 0;  // buffers of step g
+    for (int32_t g = 0; g < nsteps; ++g) {
+      fra.pin();
+      frb.pin();
+      oa.pin();
+      ob.pin();
+      // memory phase: this group's copies, the previous item's stores (after
+      // the copies, so that the waits may leave them in flight), then the
+      // fragments of step g
+      const bool stored = !EPI && kk == 0 && g > 0;
+      bool copied = false;
+      if constexpr (G == 0) {
+        if (g + 1 < nsteps) {
+          copy_b(cur, bbuf ^ 1u);
+          copied = true;
+        }
       } else {
-        if (stored) wait_vmcnt<ST, true>();
-        else wait_vmcnt<0, true>();
+        if (g + 2 < nsteps) {
+          copy_a(cur, abuf == 0 ? 2u : abuf - 1);
+          copied = true;
+        }
       }
-    } else {
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers
+      if constexpr (!EPI) {
+        if (stored) store_counted(t - 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mem(abuf, bbuf);
+      if constexpr (G == 1) {
+        // A(g + 1) has landed; A(g + 2) and the stores may still be in flight
+        if (copied) {
+          if (stored) wait_vmcnt<PA + ST, true>();
+          else wait_vmcnt<PA, true>();
+        } else {
+          if (stored) wait_vmcnt<ST, true>();
+          else wait_vmcnt<0, true>();
+        }
+      } else {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers
+      }
+      barrier();
+      if (kk == 0)
+        comp(std::true_type{});
+      else
+        comp(std::false_type{});
+      if constexpr (G == 0) {
+        if (copied) {
+          // B(g + 1) has landed; the stores issued after it may not have
+          if (stored) wait_vmcnt<ST, false>();
+          else wait_vmcnt<0, false>();
+        }
+      }
+      if (G == 0 || g + 1 < nsteps) barrier();
+      abuf = abuf == 2 ? 0u : abuf + 1;
+      bbuf ^= 1u;
+      if (++kk == nk) {
+        kk = 0;
+        ++t;
+      }
     }
-    barrier();
-    if (kk == 0)
-      comp(std::true_type{});
-    else
-      comp(std::false_type{});
-    if (grp == 0 && copied) {
-      // B(g + 1) has landed; the stores issued after it may not have
-      if (stored) wait_vmcnt<ST, false>();
-      else wait_vmcnt<0, false>();
-    }
-    if (grp == 0 || g + 1 < nsteps) barrier();
-    abuf = abuf == 2 ? 0u : abuf + 1;
-    bbuf ^= 1u;
-    if (++kk == nk) {
-      kk = 0;
-      ++t;
-    }
-  }
+  };
+  if (grp == 0)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
   if (persistent)
     store_counted(items - 1);
   else

@@ -375,7 +375,8 @@ static tg_status launch(const gemm_plan_t* plan, const gemm_epilogue_t* epi, int
                         (kTiles[tile].kind == tg::kPingPong || kTiles[tile].kind == tg::kPingPongEpi);
   if (pingpong) {
     const int64_t items = cdiv(p.m, kTiles[tile].bm) * cdiv(p.n, kTiles[tile].bn) * batch;
-    if (p.k == 0 || items >= ((int64_t)1 << 30))
+    // (its 32-bit step counters: items x K steps below 2^31)
+    if (p.k == 0 || items >= ((int64_t)1 << 30) || items * cdiv(p.k, kTiles[tile].bk) >= ((int64_t)1 << 31))
       tile = tg::kWideTile;
     else
       tile = a.epi ? tg::kPingPongEpiTile : tg::kPingPongTile;

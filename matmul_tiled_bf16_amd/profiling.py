@@ -166,6 +166,10 @@ PASSES = [
     "TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE",
     "SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_VMEM_RD "
     "SQ_INSTS_VMEM_WR SQ_WAVES",
+    # the HBM/L2 -> LDS copy path: texture address (TA) and data (TD) units, L1 (TCP)
+    "TA_TA_BUSY_sum TA_ADDR_STALLED_BY_TC_CYCLES_sum TD_TD_BUSY_sum TD_TC_STALL_sum GRBM_GUI_ACTIVE",
+    "TA_BUFFER_TOTAL_CYCLES_sum TA_DATA_STALLED_BY_TC_CYCLES_sum TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum "
+    "TCP_PENDING_STALL_CYCLES_sum TCP_TCR_TCP_STALL_CYCLES_sum GRBM_GUI_ACTIVE",
 ]
 N_XCD = 8            # MI355X: GRBM_GUI_ACTIVE reads the sum over its 8 XCDs
 N_SIMD = 256 * 4     # 256 CUs x 4 SIMDs
@@ -246,6 +250,18 @@ def counters(out_dir: str, pattern: str) -> str:
         f"MFMA {v['SQ_INSTS_MFMA'] / v['SQ_WAVES']:.0f}, SALU {v['SQ_INSTS_SALU'] / v['SQ_WAVES']:.0f}, "
         f"LDS {v['SQ_INSTS_LDS'] / v['SQ_WAVES']:.0f}, VMEM read {v['SQ_INSTS_VMEM_RD'] / v['SQ_WAVES']:.0f}, "
         f"VMEM write {v['SQ_INSTS_VMEM_WR'] / v['SQ_WAVES']:.0f}",
+        "",
+        "## copy path (TA: address unit, TD: data unit, TCP: L1; one of each per CU)",
+        f"TA busy = {100 * v['TA_TA_BUSY_sum'] / (cyc * 256):.1f} % of CU cycles, "
+        f"address path stalled by the cache {100 * v['TA_ADDR_STALLED_BY_TC_CYCLES_sum'] / (cyc * 256):.1f} %, "
+        f"data path stalled {100 * v['TA_DATA_STALLED_BY_TC_CYCLES_sum'] / (cyc * 256):.1f} %",
+        f"TA buffer cycles = {100 * v['TA_BUFFER_TOTAL_CYCLES_sum'] / (cyc * 256):.1f} % of CU cycles",
+        f"TD busy = {100 * v['TD_TD_BUSY_sum'] / (cyc * 256):.1f} %, TD waiting for cache data "
+        f"{100 * v['TD_TC_STALL_sum'] / (cyc * 256):.1f} %",
+        f"L1->L2 read latency = {v['TCP_TCC_READ_REQ_LATENCY_sum'] / v['TCP_TCC_READ_REQ_sum']:.0f} cycles per request "
+        f"({v['TCP_TCC_READ_REQ_sum']:.0f} requests)",
+        f"L1 stalled on pending L2 data = {100 * v['TCP_PENDING_STALL_CYCLES_sum'] / (cyc * 256):.1f} %, "
+        f"L1 request path stalled = {100 * v['TCP_TCR_TCP_STALL_CYCLES_sum'] / (cyc * 256):.1f} %",
     ]
     return "\n".join(lines)
 
