@@ -484,10 +484,12 @@ __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(GemmArgs args) {
   barrier();
   if (grp == 1) barrier();  // group 1 runs one phase behind
 
-  // The K-step loop, compiled once per group (the group is uniform over a
-  // wave), so that each wave's loop carries only its own copies and waits.
-  auto run = [&](auto group) {
+  // The K-step loop, compiled once per group and read/copy order (both are
+  // uniform over a wave), so that each wave's loop carries only its own
+  // copies and waits.
+  auto run = [&](auto group, auto reads_first) {
     constexpr int G = decltype(group)::value;
+    constexpr bool RF = decltype(reads_first)::value;
     int32_t kk = 0, t = 0;        // step within the item, item
     uint32_t abuf = 0, bbuf = 0;  // buffers of step g
     for (int32_t g = 0; g < nsteps; ++g) {
@@ -496,10 +498,16 @@ __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(GemmArgs args) {
       oa.pin();
       ob.pin();
       // memory phase: this group's copies, the previous item's stores (after
-      // the copies, so that the waits may leave them in flight), then the
-      // fragments of step g
+      // the copies, so that the waits may leave them in flight) and the
+      // fragments of step g -- fragments first in half of the waves (RF), so
+      // that the copy burst (which holds a wave until the address unit takes
+      // each copy) and the LDS reads proceed side by side
       const bool stored = !EPI && kk == 0 && g > 0;
       bool copied = false;
+      if constexpr (RF) {
+        mem(abuf, bbuf);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if constexpr (G == 0) {
         if (g + 1 < nsteps) {
           copy_b(cur, bbuf ^ 1u);
@@ -515,7 +523,7 @@ __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(GemmArgs args) {
         if (stored) store_counted(t - 1);
       }
       __builtin_amdgcn_sched_barrier(0);
-      mem(abuf, bbuf);
+      if constexpr (!RF) mem(abuf, bbuf);
       if constexpr (G == 1) {
         // A(g + 1) has landed; A(g + 2) and the stores may still be in flight
         if (copied) {
@@ -549,10 +557,13 @@ __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(GemmArgs args) {
       }
     }
   };
-  if (grp == 0)
-    run(std::integral_constant<int, 0>{});
-  else
-    run(std::integral_constant<int, 1>{});
+  if (grp == 0) {
+    if (sw < 2) run(std::integral_constant<int, 0>{}, std::false_type{});
+    else run(std::integral_constant<int, 0>{}, std::true_type{});
+  } else {
+    if (sw < 2) run(std::integral_constant<int, 1>{}, std::false_type{});
+    else run(std::integral_constant<int, 1>{}, std::true_type{});
+  }
   if (persistent)
     store_counted(items - 1);
   else
