@@ -19,7 +19,7 @@ Workloads (seeded synthetic inputs from synth/):
                 in one grouped launch; also times one launch per problem
   splitk_long   1024 x 1024 x 65536 NN, bf16 out, K split into parts (gemm_splitk_run);
                 also times the same product as one plain launch
-  ragged_1000   1000^3 NN, fp32 out
+  ragged_1000   1000^3 NN, fp32 out (ragged_1000_nt / _tn / _tt: the other layouts)
   square_256    256^3 NN, fp32 out
 
 The "roofline" object rates the dominant kernel against MI355X's published
@@ -57,6 +57,8 @@ def problems(name):
         return synth.attention_bmm()[1:]
     if name == "ragged_1000":
         return synth.ragged_1000()[:1]
+    if name in ("ragged_1000_nt", "ragged_1000_tn", "ragged_1000_tt"):
+        return [q for q in synth.ragged_1000() if q.name == name]
     if name == "square_256":
         return synth.square_256()
     raise SystemExit(f"unknown workload {name}")
@@ -83,6 +85,8 @@ def main():
     ap.add_argument("--beta", type=float, default=0.0, help="epilogue: scale of C's prior contents")
     ap.add_argument("--bias", action="store_true", help="epilogue: add a per-column bias")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration measurements added to the default run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to calibrate FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
@@ -233,9 +237,179 @@ def main():
                      "launches_queued_ahead": bool(queued_ahead),
                      "algorithmic": {"flops": flops, "bytes": nbytes}},
     }
+    line["clock"] = clock_during(torch, stream, step, kernel_s)
+    if args.workload == "square_8192" and not args.no_configs and not epi and args.tile is None:
+        line["configs"] = run_configs(torch, tg, profiling)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(p, unit, args.cpu_seconds)
+        line["cpu_baseline"].update(cpu_context())
     print(json.dumps(line), flush=True)
+
+
+def clock_during(torch, stream, step, kernel_s, seconds=1.5):
+    """Shader clock and board power sampled (amdsmi, every ~20 ms) while the
+    GPU runs about `seconds` of back-to-back launches of the timed step.
+    The timed region itself (tens of ms) is too short to sample; this window
+    runs the same launches right after it.  None if amdsmi is unavailable."""
+    import threading
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception as e:  # no amdsmi library or no driver access
+        return {"error": f"amdsmi unavailable: {type(e).__name__}"}
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        h = handles[0]
+        try:
+            bus = torch.cuda.get_device_properties(0).pci_bus_id
+            for c in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(c)
+                if int(bdf.split(":")[1], 16) == bus:
+                    h = c
+                    break
+        except Exception:
+            pass
+        cap = amdsmi.amdsmi_get_power_cap_info(h).get("power_cap")
+        samples, stop = [], threading.Event()
+
+        def poll():
+            while not stop.is_set():
+                try:
+                    clk = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"]
+                    pw = amdsmi.amdsmi_get_power_info(h)
+                    samples.append((float(clk), float(pw.get("socket_power") or pw.get("current_socket_power"))))
+                except Exception:
+                    pass
+                stop.wait(0.02)
+
+        n = max(16, int(seconds / max(kernel_s, 1e-6)))
+        th = threading.Thread(target=poll, daemon=True)
+        torch.cuda.synchronize()
+        th.start()
+        for i in range(n):
+            step(i)
+        torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        # drop the first 10% (the clock settles after the launches start)
+        body = samples[len(samples) // 10:] or samples
+        if not body:
+            return {"error": "no samples"}
+        clk = sorted(c for c, _ in body)
+        pw = sorted(w for _, w in body)
+        med = lambda v: v[len(v) // 2]
+        return {"sclk_mhz_median": med(clk), "sclk_mhz_min": clk[0], "sclk_mhz_max": clk[-1],
+                "power_w_median": med(pw), "power_w_max": pw[-1],
+                "power_cap_w": (cap / 1e6 if cap and cap > 1e5 else cap), "samples": len(body),
+                "window": f"{n} back-to-back launches after the timed region"}
+    except Exception as e:
+        return {"error": f"{type(e).__name__}: {e}"}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+
+def run_configs(torch, tg, profiling):
+    """Every other configuration of the workload set, each on its own seeded
+    inputs: kernel time per launch (HIP events around back-to-back launches
+    queued while the stream is held), rate, and the fraction of the peak of
+    its binding roofline.  HBM-bound products cycle through copies of B (or of
+    their large operand) so that each launch reads from HBM, not from the
+    256 MiB Infinity Cache."""
+    import synth
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    out = {}
+    sets = [("square_256", synth.square_256(), 200), ("ragged_1000", synth.ragged_1000(), 200),
+            ("skinny_16", synth.skinny_16(), 200), ("attention_bmm", synth.attention_bmm(), 20)]
+    for _, probs, steps in sets:
+        for p in probs:
+            tin = torch.bfloat16 if p.in_dtype == "bf16" else torch.float16
+            tout = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[p.out_dtype]
+            osz = 4 if p.out_dtype == "fp32" else 2
+            up = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(tin).to(dev)
+            flops = roofline_flops(p)
+            nbytes = p.batch * ((p.m * p.k + p.k * p.n) * 2 + p.m * p.n * osz)
+            bound = "mfma" if flops / nbytes >= PEAK_MFMA / PEAK_HBM else "hbm"
+            # the operand that dominates the bytes is rotated for HBM-bound products
+            big_a = p.A.size > p.B.size
+            # small products are measured hot (their operands stay in the caches, as they
+            # would between back-to-back calls); large HBM-bound ones from HBM
+            small = p.name.startswith(("square_256", "ragged_1000"))
+            copies = 4 if bound == "hbm" and not small else 1
+            if p.name.startswith("attn_s"):
+                copies = 1  # 2 GiB of output per launch: nothing of it stays in a cache
+            A0, B0 = up(p.A), up(p.B)
+            As = [A0] + [A0.clone() for _ in range(copies - 1)] if big_a else [A0]
+            Bs = [B0] + [B0.clone() for _ in range(copies - 1)] if not big_a else [B0]
+            C = torch.empty((p.batch, p.m, p.n) if p.batch > 1 else (p.m, p.n), dtype=tout, device=dev)
+            pl = tg.plan(p.m, p.n, p.k, trans_a=p.trans_a, trans_b=p.trans_b, in_dtype=tin, out_dtype=tout,
+                         lda=p.lda, ldb=p.ldb, ldc=p.ldc, batch=p.batch)
+
+            def step(i, pl=pl, As=As, Bs=Bs, C=C, p=p):
+                A, B = As[i % len(As)], Bs[i % len(Bs)]
+                if p.batch == 1:
+                    tg.gemm_run(pl, A, B, C, stream)
+                else:
+                    tg.bmm_run(pl, p.batch, p.stride_a, p.stride_b, p.stride_c, A, B, C, stream)
+
+            for i in range(5):
+                step(i)
+            torch.cuda.synchronize()
+            mean_ms, kms, ahead = gated_kernel_ms(torch, stream, step, steps, 5)
+            assert torch.isfinite(C.float()).all().item(), f"{p.name}: non-finite output"
+            s = mean_ms / 1e3
+            rate = flops / s / 1e12 if bound == "mfma" else nbytes / s / 1e9
+            peak = PEAK_MFMA / 1e12 if bound == "mfma" else PEAK_HBM / 1e9
+            out[p.name] = {
+                "m": p.m, "n": p.n, "k": p.k, "batch": p.batch,
+                "op": ("T" if p.trans_a else "N") + ("T" if p.trans_b else "N"),
+                "out_dtype": p.out_dtype, "kernel_us": round(mean_ms * 1e3, 2),
+                "kernel_us_each_min": round(float(np.min(kms)) * 1e3, 2),
+                "tflops": round(flops / s / 1e12, 2), "gbps": round(nbytes / s / 1e9, 1),
+                "bound": bound, "frac": round(rate / peak, 4),
+                "operand_copies": copies, "hot_cache": small, "launches": steps, "queued_ahead": bool(ahead),
+                "tile_index": int(pl.tile), "variant": int(pl.variant),
+                "traffic": profiling.read_traffic(p.name),
+                "algorithmic": {"flops": flops, "bytes": nbytes}}
+            del As, Bs, C, A0, B0
+            torch.cuda.empty_cache()
+    return out
+
+
+def roofline_flops(p):
+    return 2 * p.m * p.n * p.k * p.batch
+
+
+def cpu_context():
+    """The host CPU model, and the oracle on the full 256^3 product on one
+    thread (a child process, so that the thread count is its own)."""
+    import subprocess
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    code = ("import time, synth, oracle\n"
+            "(p,) = synth.square_256()\n"
+            "oracle.gemm_problem(p)\n"
+            "t0 = time.perf_counter(); oracle.gemm_problem(p); t = time.perf_counter() - t0\n"
+            "print(2 * 256 ** 3 / t / 1e9)\n")
+    single = None
+    try:
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                           timeout=120)
+        single = round(float(r.stdout.strip().splitlines()[-1]), 3)
+    except Exception:
+        pass
+    return {"cpu_model": model, "single_thread_square_256_gflops": single}
 
 
 def run_attention(args, torch, tg, profiling):
