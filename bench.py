@@ -10,6 +10,7 @@ synchronisations.  Prints one JSON line.
 
 Workloads (seeded synthetic inputs from synth/):
   square_8192   8192^3, NN, bf16 in, bf16 out        (default; MFMA-bound)
+  square_8192_nt / _tn / _tt   the same product under the other op() layouts
   skinny_16     M=16, N=K=8192, B stored N x K, bf16 out  (HBM-bound)
   attention_s   128 x (2048x2048x128) S = Q K^T, fp32 out (HBM-bound)
   attention_o   128 x (2048x128x2048) O = P V,   fp32 out (HBM-bound)
@@ -49,6 +50,8 @@ def problems(name):
     import synth
     if name == "square_8192":
         return synth.square_8192()
+    if name in ("square_8192_nt", "square_8192_tn", "square_8192_tt"):
+        return synth.square_8192(layout=name[-2:])
     if name == "skinny_16":
         return synth.skinny_16()
     if name == "attention_s":
@@ -246,11 +249,17 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def clock_during(torch, stream, step, kernel_s, seconds=1.5):
-    """Shader clock and board power sampled (amdsmi, every ~20 ms) while the
-    GPU runs about `seconds` of back-to-back launches of the timed step.
-    The timed region itself (tens of ms) is too short to sample; this window
-    runs the same launches right after it.  None if amdsmi is unavailable."""
+def clock_during(torch, stream, step, kernel_s, seconds=3.0):
+    """Shader clock and board power while the GPU runs about `seconds` of
+    back-to-back launches of the timed step (the timed region itself is too
+    short to sample; this window runs the same launches right after it).
+
+    The driver's metrics table (amdsmi_get_gpu_metrics_info) refreshes only a
+    few times a second, so every poll inside the window is not a new reading:
+    only refreshes first seen after the clock settled (0.3 s in) and before
+    the GPU went idle count, one sample per distinct firmware timestamp.
+    Reports the clock of the first XCD and the spread over the eight XCDs.
+    None of it if amdsmi is unavailable."""
     import threading
     try:
         import amdsmi
@@ -270,14 +279,20 @@ def clock_during(torch, stream, step, kernel_s, seconds=1.5):
         except Exception:
             pass
         cap = amdsmi.amdsmi_get_power_cap_info(h).get("power_cap")
-        samples, stop = [], threading.Event()
+        polls, stop = [], threading.Event()
+        t00 = time.perf_counter()
+
+        def num(v):
+            return float(v) if isinstance(v, (int, float)) else None
 
         def poll():
             while not stop.is_set():
                 try:
-                    clk = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"]
-                    pw = amdsmi.amdsmi_get_power_info(h)
-                    samples.append((float(clk), float(pw.get("socket_power") or pw.get("current_socket_power"))))
+                    m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                    xcds = [num(c) for c in (m.get("current_gfxclks") or [])]
+                    xcds = [c for c in xcds if c is not None and c < 65535]
+                    polls.append((time.perf_counter() - t00, m.get("firmware_timestamp"), num(m.get("current_gfxclk")),
+                                  xcds, num(m.get("current_socket_power"))))
                 except Exception:
                     pass
                 stop.wait(0.02)
@@ -286,22 +301,33 @@ def clock_during(torch, stream, step, kernel_s, seconds=1.5):
         th = threading.Thread(target=poll, daemon=True)
         torch.cuda.synchronize()
         th.start()
+        time.sleep(0.05)
+        t_start = time.perf_counter() - t00
         for i in range(n):
             step(i)
         torch.cuda.synchronize()
+        t_end = time.perf_counter() - t00
         stop.set()
         th.join()
-        # drop the first 10% (the clock settles after the launches start)
-        body = samples[len(samples) // 10:] or samples
+        seen, body = set(), []
+        for t, stamp, clk, xcds, pw in polls:
+            key = stamp if stamp is not None else (clk, tuple(xcds), pw)
+            if key in seen:
+                continue
+            seen.add(key)
+            if t_start + 0.3 <= t <= t_end - 0.02 and clk is not None and pw is not None:
+                body.append((clk, xcds, pw))
         if not body:
-            return {"error": "no samples"}
-        clk = sorted(c for c, _ in body)
-        pw = sorted(w for _, w in body)
+            return {"error": "no metrics refresh inside the launch window", "polls": len(polls)}
+        clk = sorted(c for c, _, _ in body)
+        pw = sorted(w for _, _, w in body)
+        xall = sorted(x for _, xs, _ in body for x in xs)
         med = lambda v: v[len(v) // 2]
         return {"sclk_mhz_median": med(clk), "sclk_mhz_min": clk[0], "sclk_mhz_max": clk[-1],
+                "sclk_mhz_xcd_min": xall[0] if xall else None, "sclk_mhz_xcd_max": xall[-1] if xall else None,
                 "power_w_median": med(pw), "power_w_max": pw[-1],
-                "power_cap_w": (cap / 1e6 if cap and cap > 1e5 else cap), "samples": len(body),
-                "window": f"{n} back-to-back launches after the timed region"}
+                "power_cap_w": (cap / 1e6 if cap and cap > 1e5 else cap), "refreshes": len(body),
+                "window": f"{n} back-to-back launches after the timed region, {t_end - t_start:.2f} s"}
     except Exception as e:
         return {"error": f"{type(e).__name__}: {e}"}
     finally:

@@ -167,11 +167,14 @@ def attention_bmm(seed: int = 3, batch: int = 128, seq: int = 2048, head: int = 
     return [s, o]
 
 
-def square_8192(seed: int = 4, out_dtype: str = "bf16") -> List[Problem]:
+def square_8192(seed: int = 4, out_dtype: str = "bf16", layout: str = "nn") -> List[Problem]:
+    """8192^3 with both operands drawn N(0, 1); ``layout`` picks op(A) op(B)
+    (the stored arrays are square, so every layout reads the same draws)."""
     rng = np.random.default_rng(seed)
     A = draw(rng, (8192, 8192), "normal", 1.0)
     B = draw(rng, (8192, 8192), "normal", 1.0)
-    return [Problem("square_8192_nn", A, B, 0, 0, 8192, 8192, 8192, out_dtype=out_dtype)]
+    ta, tb = int(layout[0] == "t"), int(layout[1] == "t")
+    return [Problem(f"square_8192_{layout}", A, B, ta, tb, 8192, 8192, 8192, out_dtype=out_dtype)]
 
 
 def long_k(seed: int = 10, m: int = 1024, n: int = 1024, k: int = 65536, out_dtype: str = "bf16") -> List[Problem]:
