@@ -13,13 +13,14 @@ namespace {
 using tg::AttnArgs;
 using tg::AttnFn;
 
-// One launch shape per head dimension: 4 waves of 32 query rows, 64 keys per
-// stage, 2 stages (64 KiB of LDS at d = 128, so two work-groups share a CU).
-constexpr int kWaves = 4, kRB = 1, kBN = 64, kStages = 2;
+// One launch shape per head dimension: the ping-pong kernel's 8 waves of 32
+// query rows (256 per work-group), 64-key blocks, rings of 4 K and 5 V blocks
+// (144 KiB of LDS at d = 128: one work-group per CU).
+constexpr int kWaves = 8, kBN = 64, kRingK = 4, kRingV = 5;
 
 template <typename In, typename Out, int D>
 constexpr AttnFn attn_kernel() {
-  return tg::attn_fwd_kernel<In, Out, D, kWaves, kRB, kBN, kStages>;
+  return tg::attn_pp_kernel<In, Out, D>;
 }
 
 // [in bf16/fp16][out fp32/same][d 64/128]
@@ -29,7 +30,7 @@ const AttnFn kAttn[2][2][2] = {
     {{attn_kernel<_Float16, float, 64>(), attn_kernel<_Float16, float, 128>()},
      {attn_kernel<_Float16, _Float16, 64>(), attn_kernel<_Float16, _Float16, 128>()}}};
 
-constexpr uint32_t lds_bytes(int d) { return (uint32_t)kStages * 2u * kBN * 2u * (uint32_t)d; }
+constexpr uint32_t lds_bytes(int d) { return (uint32_t)(kRingK + kRingV) * kBN * 2u * (uint32_t)d; }
 
 }  // namespace
 
@@ -66,7 +67,7 @@ tg_status attention_fwd(tg_dtype in_type, tg_dtype out_type, int64_t batch, int6
                                        stride_o % 8 == 0));
   if (!aligned) return TG_ERR_UNSUPPORTED;
 
-  constexpr int BM = 32 * kRB * kWaves;
+  constexpr int BM = 32 * kWaves;
   const int64_t q_blocks = (n_q + BM - 1) / BM;
   if (q_blocks >= ((int64_t)1 << 31)) return TG_ERR_INVALID;
   const int64_t total = q_blocks * batch;

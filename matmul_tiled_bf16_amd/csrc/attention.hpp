@@ -10,16 +10,15 @@
 // O once, so the pair's HBM traffic drops from ~4*n_q*n_k bytes per head to
 // ~2*(n_q + 2*n_k)*d and the launch becomes bound by the matrix cores.
 //
-//  * Work: one work-group owns BM = 32*WAVES query rows of one head; each
-//    wave owns 32 rows.  Work items are (head, row block) pairs decoded in
-//    XCD-contiguous runs, so the row blocks of one head -- which all read
-//    that head's K and V -- meet in one XCD's L2.
+//  * Work items are (head, 256-row block) pairs decoded in XCD-contiguous
+//    runs, so the row blocks of one head -- which all read that head's K and
+//    V -- meet in one XCD's L2.
 //  * Q: each lane keeps its query row's fragment for every 16-wide step of d
 //    (8 elements, 16 bytes, per step) in registers for the whole item.
-//  * K, V: BN keys at a time go HBM -> LDS by direct-to-LDS buffer loads into
-//    a ring of S stages (the tile kernel's copy primitive and swizzles: K
-//    rows are d-contiguous and read with ds_read_b128, V rows are read with
-//    the transposing ds_read_b64_tr_b16).  Rows past n_k read as zero.
+//  * K, V: 64 keys at a time go HBM -> LDS by direct-to-LDS buffer loads (the
+//    tile kernel's copy primitive and swizzles: K rows are d-contiguous and
+//    read with ds_read_b128, V rows are read with the transposing
+//    ds_read_b64_tr_b16).  Rows past n_k read as zero.
 //  * Scores: v_mfma_f32_32x32x16 with K as the first operand and Q as the
 //    second gives S^T: lane l holds query row l&31 and, per 32-key block,
 //    keys 8g + 4(l>>5) + {0..3}, g = 0..3; lanes l and l^32 share a row.
@@ -58,43 +57,64 @@ struct AttnArgs {
 
 using AttnFn = void (*)(AttnArgs);
 
-// D: head dimension; WAVES: waves per work-group; RB: 32-row query blocks per
-// wave (each K or V fragment read from LDS feeds RB MFMAs); BN: keys per
-// stage; S: LDS stages.  RB = 1 runs two waves per SIMD (the softmax of one
-// overlaps the MFMAs of the other); RB = 2 needs the whole register file
-// (O alone is 128 registers per lane) and runs one.
-template <typename In, typename Out, int D, int WAVES, int RB, int BN, int S>
-__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1)))
-attn_fwd_kernel(AttnArgs a) {
+// The kernel: eight waves in two groups of four; the dispatcher puts waves w
+// and w + 4 on one SIMD, so each SIMD holds one wave of each group.  Wave w
+// owns query rows [32 w, 32 w + 32) of a 256-row block.  A group alternates
+// two phases, one work-group barrier after each:
+//
+//   MFMA phase i    : O += P(i-1) V(i-1), then S(i) = K(i) Q^T, with the V and
+//                     K fragments read from LDS a few MFMAs ahead of use;
+//   softmax phase i : the copies of key block i + 3, then the online softmax
+//                     of S(i) into P(i) (registers only).
+//
+// Group 1 runs one phase behind group 0, so on every SIMD one wave issues
+// back-to-back MFMAs while the other does the exponentials, and the matrix
+// core waits only at the turn.  This is the pages' warp-specialised pipeline
+// ("FLA Triton -> Gluon Porting Skill", section 5) with the two waves that
+// share a SIMD, as the ping-pong GEMM kernel does for its copies.
+//
+//  * K blocks (64 keys) go through a ring of four LDS slots and V blocks
+//    through a ring of five.  Every wave issues its share of block i + 3 in
+//    its softmax phase i: K(i+3) into the slot of K(i-1), last read in group
+//    1's MFMA phase i - 1, and V(i+3) into the slot of V(i-2), last read in
+//    the same phase; both closed before the barrier that opened phase i.
+//  * Before the barrier that ends global phase 2i + 1 every wave's share of
+//    block i + 1 has landed: group 0 (end of its softmax phase i) may leave
+//    blocks i + 2 and i + 3 in flight, group 1 (end of its MFMA phase i)
+//    block i + 2.
+//  * Registers: O (64), the Q fragments (32), S (32) and P (16) per lane; the
+//    fragments in flight stay a few MFMAs deep, so nothing spills (a spill
+//    reload would wait for every copy in flight).
+template <typename In, typename Out, int D>
+__global__ void __launch_bounds__(512) attn_pp_kernel(AttnArgs a) {
   static_assert(D == 64 || D == 128, "head dimension 64 or 128");
-  static_assert(RB == 1 || RB == 2, "one or two row blocks per wave");
-  static_assert(BN % 32 == 0 && S >= 2 && S <= 4, "stage shape");
-  constexpr int WR = 32 * RB;            // query rows per wave
-  constexpr int BM = WR * WAVES;         // query rows per work-group
-  constexpr int ROWB = 2 * D;            // bytes of one K or V row
-  constexpr int DCH = D / 8;             // 16-byte units per row
-  constexpr int TI = BN * ROWB / 1024;   // 1 KiB wave copies per K (or V) tile
-  static_assert(TI % WAVES == 0, "tile copies split evenly over the waves");
-  constexpr int PW = TI / WAVES;         // per wave, per tile
+  constexpr int NW = 8, BN = 64, RK = 4, RV = 5;  // waves, keys per block, ring slots
+  constexpr int BM = 32 * NW;                     // query rows per work-group
+  constexpr int ROWB = 2 * D;                     // bytes of one K or V row
+  constexpr int DCH = D / 8;                      // 16-byte units per row
+  constexpr int TI = BN * ROWB / 1024;            // 1 KiB wave copies per K (or V) block
+  static_assert(TI % NW == 0, "block copies split evenly over the waves");
+  constexpr int PW = TI / NW;                     // per wave, per block and operand
+  constexpr int C = 2 * PW;                       // per wave, per block
   constexpr uint32_t TILE = BN * ROWB;
-  constexpr uint32_t STAGE = 2 * TILE;   // K tile, then V tile
-  constexpr int NKB = BN / 32;           // 32-key score blocks per stage
-  constexpr int DS = D / 16;             // 16-wide d steps of Q K^T
-  constexpr int DB = D / 32;             // 32-wide d blocks of O
-  constexpr int KS = BN / 16;            // 16-key steps of P V
-  constexpr float TAU = 8.f;             // log2 headroom before m is raised
+  constexpr int NKB = BN / 32;                    // 32-key score blocks
+  constexpr int DS = D / 16;                      // 16-wide d steps of Q K^T
+  constexpr int DB = D / 32;                      // 32-wide d blocks of O
+  constexpr int KS = BN / 16;                     // 16-key steps of P V
+  constexpr int NV = KS * DB, NK = DS * NKB;      // MFMAs of P V and of Q K^T
+  constexpr int FP = 4;                           // fragments read ahead of their MFMA
+  constexpr float TAU = 8.f;
 
   extern __shared__ __attribute__((aligned(1024))) char tg_smem[];
   TG_LDS char* lds = (TG_LDS char*)tg_smem;
-  const uint32_t lds0 = (uint32_t)(size_t)lds;
+  const uint32_t lds0 = (uint32_t)(size_t)lds;  // K ring, then V ring
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2;
   const int li = lane & 31, lg = lane >> 5;
   const int trh = lane >> 4, trs = lane & 15;
 
-  // this wave's share of a tile copy: instruction i covers tile bytes
-  // (wave*PW + i)*1024 + 16*lane; the swizzle picks the source unit
   uint32_t koff[PW], voff[PW];
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
@@ -103,9 +123,19 @@ attn_fwd_kernel(AttnArgs a) {
     koff[i] = (uint32_t)(row * a.ldk * 2) + ((phys ^ swz_unit<true, DCH>(row)) << 4);
     voff[i] = (uint32_t)(row * a.ldv * 2) + ((phys ^ swz_unit<false, DCH>(row)) << 4);
   }
+  // LDS offsets of this lane's fragment reads: K step ks at rows li (+32 kb,
+  // a constant), V block db at rows 4 lg + (trs >> 2) (+16 t and +8, constants:
+  // the swizzles depend on the row only through bits the constants leave alone)
+  uint32_t kof[DS], vof[DB];
+#pragma unroll
+  for (int ks = 0; ks < DS; ++ks) kof[ks] = swz_off<true, DCH>(li, ks * 16 + lg * 8);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    vof[db] = swz_off<false, DCH>(4 * lg + (trs >> 2), db * 32 + 16 * (trh & 1) + 4 * (trs & 3));
 
   const int64_t total = (int64_t)a.q_blocks * a.batch;
-  const int64_t nkb = (a.n_k + BN - 1) / BN;
+  const int32_t nkb = (int32_t)((a.n_k + BN - 1) / BN);
+  const bool ragged = a.n_k % BN != 0;
 
   for (int64_t w0 = blockIdx.x; w0 < total; w0 += gridDim.x) {
     int64_t b;
@@ -116,185 +146,218 @@ attn_fwd_kernel(AttnArgs a) {
     const uint16_t* Kh = a.K + b * a.sk;
     const uint16_t* Vh = a.V + b * a.sv;
 
-    // copies of key block j into stage s
-    auto issue = [&](int64_t j, int s) {
-      const int64_t k0 = j * BN;
+    auto issue = [&](int32_t j) __attribute__((always_inline)) {
+      const int64_t k0 = (int64_t)j * BN;
       const int64_t valid = min((int64_t)BN, a.n_k - k0);
       const i32x4 rk = make_rsrc(Kh + k0 * a.ldk, ((valid - 1) * a.ldk + D) * 2);
       const i32x4 rv = make_rsrc(Vh + k0 * a.ldv, ((valid - 1) * a.ldv + D) * 2);
-      const uint32_t st = lds0 + (uint32_t)s * STAGE + (uint32_t)(wave * PW) * 1024u;
+      const uint32_t part = (uint32_t)(wave * PW) * 1024u;
+      const uint32_t ks = lds0 + (uint32_t)(j % RK) * TILE + part;
+      const uint32_t vs = lds0 + RK * TILE + (uint32_t)(j % RV) * TILE + part;
 #pragma unroll
-      for (int i = 0; i < PW; ++i) dma16(rk, koff[i], st + (uint32_t)i * 1024u);
+      for (int i = 0; i < PW; ++i) dma16(rk, koff[i], ks + (uint32_t)i * 1024u);
 #pragma unroll
-      for (int i = 0; i < PW; ++i) dma16(rv, voff[i], st + TILE + (uint32_t)i * 1024u);
+      for (int i = 0; i < PW; ++i) dma16(rv, voff[i], vs + (uint32_t)i * 1024u);
     };
 
-    // Q fragments of this lane's rows: row block rb, d = 16 ks + 8 lg .. +7
-    u32x4 qf[RB][DS];
+    // Q fragments of this lane's row: d = 16 ks + 8 lg .. +7 (loaded before
+    // the first copies, so the first counted wait covers them)
+    u32x4 qf[DS];
     {
       const __amdgpu_buffer_rsrc_t rq =
           store_rsrc(a.Q + b * a.sq + q0 * a.ldq, ((rows_q - 1) * a.ldq + D) * 2);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const uint32_t ro = (uint32_t)((wave * WR + rb * 32 + li) * a.ldq * 2);
-#pragma unroll
-        for (int ks = 0; ks < DS; ++ks)
-          qf[rb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rq, (int)(ro + (uint32_t)(16 * ks + 8 * lg) * 2), 0, 0));
-      }
-    }
-
-#pragma unroll
-    for (int s = 0; s < S - 1; ++s)
-      if (s < nkb) issue(s, s);
-
-    f32x16 o[RB][DB];
-    float m[RB], l[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-      for (int i = 0; i < DB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[rb][i][r] = 0.f;
-      m[rb] = -__builtin_inff();  // running maximum, log2 units
-      l[rb] = 0.f;                // this lane's share of the row sum
-    }
-
-    for (int64_t j = 0; j < nkb; ++j) {
-      // own copies of block j have landed (later blocks may still be in
-      // flight); the barrier publishes everyone's and frees stage (j-1) % S
-      wait_steps<2 * PW, true>(min((int64_t)(S - 2), nkb - 1 - j));
-      block_barrier();
-      if (j + S - 1 < nkb) issue(j + S - 1, (int)((j + S - 1) % S));
-      const TG_LDS char* kt = lds + (uint32_t)(j % S) * STAGE;
-      const TG_LDS char* vt = kt + TILE;
-
-      // K fragments of the whole stage, all in flight before the first MFMA
-      u32x4 kf[DS][NKB];
+      const uint32_t ro = (uint32_t)((wave * 32 + li) * a.ldq * 2);
 #pragma unroll
       for (int ks = 0; ks < DS; ++ks)
+        qf[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rq, (int)(ro + (uint32_t)(16 * ks + 8 * lg) * 2), 0, 0));
+    }
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          kf[ks][kb] = lds_read16(kt, swz_off<true, DCH>(kb * 32 + li, ks * 16 + lg * 8));
+    for (int s = 0; s < 3; ++s)
+      if (s < nkb) issue(s);
 
-      // scores S^T for BN keys x 32 query rows, per row block
-      f32x16 sc[RB][NKB];
+    f32x16 o[DB], sc[NKB];
+    u32x4 pf[KS];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+    for (int i = 0; i < DB; ++i)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sc[rb][kb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < DS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) sc[rb][kb] = mfma32<In>(kf[ks][kb], qf[rb][ks], sc[rb][kb]);
+      for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+    float m = -__builtin_inff(), l = 0.f;
 
-      // V fragments, in flight while the softmax runs: lane half lg supplies
-      // keys 16t + 4lg + {0..3} and 16t + 8 + 4lg + {0..3} of step t
-      u32x4 vf[KS][DB];
-#pragma unroll
-      for (int t = 0; t < KS; ++t)
+    // MFMA phase: MFMA q < NV is P V step (t, db) = (q / DB, q % DB) on
+    // V(i-1); q >= NV is Q K^T step (ks, kb) on K(i).  Fragment q is read
+    // FP MFMAs ahead.  WITH_PV / WITH_QK select the parts.
+    auto mfma_phase = [&](int32_t i, auto with_pv, auto with_qk) __attribute__((always_inline)) {
+      constexpr bool PV = decltype(with_pv)::value, QK = decltype(with_qk)::value;
+      constexpr int Q0 = PV ? 0 : NV, Q1 = QK ? NV + NK : NV;
+      // this phase's read bases, opaque to the compiler so that the constant
+      // parts of the offsets stay in the instructions' offset fields
+      const uint32_t vt = lds0 + RK * TILE + (uint32_t)((i + RV - 1) % RV) * TILE;
+      const uint32_t kt = lds0 + (uint32_t)(i % RK) * TILE;
+      uint32_t vb[DB], kb0[DS];
+      if constexpr (PV) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int col = db * 32 + 16 * (trh & 1) + 4 * (trs & 3);
-          const int kr = t * 16 + 4 * lg + (trs >> 2);
-          const u32x2 lo = lds_read_tr(vt, swz_off<false, DCH>(kr, col));
-          const u32x2 hi = lds_read_tr(vt, swz_off<false, DCH>(kr + 8, col));
-          vf[t][db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          vb[db] = vt + vof[db];
+          asm volatile("" : "+v"(vb[db]));
         }
-      __builtin_amdgcn_sched_barrier(0);
-
-      // keys past n_k (last block only) take no weight; lane half lg holds
-      // key kb*32 + 8(r>>2) + 4lg + (r&3) in register r
-      const int valid = (int)min((int64_t)BN, a.n_k - j * BN);
-      if (valid < BN) {
-        const int thr = valid - 4 * lg;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (kb * 32 + 8 * (r >> 2) + (r & 3) >= thr) sc[rb][kb][r] = -__builtin_inff();
       }
-
-      u32x4 pf[RB][KS];
+      if constexpr (QK) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        // row maximum over this block (both lane halves)
-        float mx = sc[rb][0][0];
+        for (int ks = 0; ks < DS; ++ks) {
+          kb0[ks] = kt + kof[ks];
+          asm volatile("" : "+v"(kb0[ks]));
+        }
+      }
+      u32x4 fr[NV + NK];
+      auto load = [&](int q) __attribute__((always_inline)) {
+        if (q < NV) {
+          const int t = q / DB, db = q % DB;
+          const TG_LDS char* v = (const TG_LDS char*)(size_t)vb[db];
+          const u32x2 lo = lds_read_tr(v, (uint32_t)(t * 16 * ROWB));
+          const u32x2 hi = lds_read_tr(v, (uint32_t)((t * 16 + 8) * ROWB));
+          fr[q] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+          const int ks = (q - NV) / NKB, kb = (q - NV) % NKB;
+          fr[q] = lds_read16((const TG_LDS char*)(size_t)kb0[ks], (uint32_t)(kb * 32 * ROWB));
+        }
+      };
+      if constexpr (QK) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[rb][kb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mxs = mx * a.c;
-        if (__builtin_amdgcn_ballot_w64(mxs > m[rb] + TAU)) {
-          const float mn = fmaxf(m[rb], mxs);
-          const float alpha = __builtin_amdgcn_exp2f(m[rb] - mn);
-          m[rb] = mn;
-          l[rb] *= alpha;
-#pragma unroll
-          for (int i = 0; i < DB; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[rb][i][r] *= alpha;
-        }
-        // probabilities (unnormalised) and their row sum (four partial sums)
-        float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          float p[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rb][kb][r], a.c, -m[rb]));
-            ls[r & 3] += p[r];
-          }
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            pf[rb][2 * kb + h] =
-                u32x4{pack2<In>(p[8 * h], p[8 * h + 1]), pack2<In>(p[8 * h + 2], p[8 * h + 3]),
-                      pack2<In>(p[8 * h + 4], p[8 * h + 5]), pack2<In>(p[8 * h + 6], p[8 * h + 7])};
-        }
-        l[rb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+          for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
       }
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = Q0; q < Q0 + FP && q < Q1; ++q) load(q);
+#pragma unroll
+      for (int q = Q0; q < Q1; ++q) {
+        if (q + FP < Q1) load(q + FP);
+        if (q < NV) {
+          const int t = q / DB, db = q % DB;
+          o[db] = mfma32<In>(fr[q], pf[t], o[db]);
+        } else {
+          const int ks = (q - NV) / NKB, kb = (q - NV) % NKB;
+          sc[kb] = mfma32<In>(fr[q], qf[ks], sc[kb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
 
-      // O += P V
+    // softmax phase i: copies of block i + 3, then P(i) from S(i).  Keys
+    // past n_k (a partial last block) take no weight; the branch is kept a
+    // branch (the asm statement stops it being if-converted into selects
+    // that every block would execute)
+    auto softmax_phase = [&](int32_t i) __attribute__((always_inline)) {
+      if (i + 3 < nkb) issue(i + 3);
+      if (ragged && i == nkb - 1) {
+        asm volatile("" ::: "memory");
+        const int thr = (int)(a.n_k - (int64_t)i * BN) - 4 * lg;
 #pragma unroll
-      for (int t = 0; t < KS; ++t)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= thr) sc[kb][r] = -__builtin_inff();
+      }
+      float mx = sc[0][0];
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma32<In>(vf[t][db], pf[rb][t], o[rb][db]);
-    }
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mxs = mx * a.c;
+      if (__builtin_amdgcn_ballot_w64(mxs > m + TAU)) {
+        asm volatile("" ::: "memory");  // a branch, not 64 multiplies per block
+        const float mn = fmaxf(m, mxs);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        m = mn;
+        l *= alpha;
+#pragma unroll
+        for (int d = 0; d < DB; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+      }
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], a.c, -m));
+          ls[r & 3] += p[r];
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          pf[2 * kb + h] = u32x4{pack2<In>(p[8 * h], p[8 * h + 1]), pack2<In>(p[8 * h + 2], p[8 * h + 3]),
+                                 pack2<In>(p[8 * h + 4], p[8 * h + 5]), pack2<In>(p[8 * h + 6], p[8 * h + 7])};
+      }
+      l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
 
-    // normalise and store: register r of o[rb][db] is
-    // O[row rb*32 + li][db*32 + 8(r>>2) + 4 lg + (r&3)]
+    // counted waits: block i + 1 complete, `later` blocks' copies may stay
+    // in flight; LDS reads drained
+    auto wait_blocks = [&](int32_t later) __attribute__((always_inline)) {
+      if (later >= 2) wait_vmcnt<2 * C, true>();
+      else if (later == 1) wait_vmcnt<C, true>();
+      else wait_vmcnt<0, true>();
+    };
+
+    // One key block for this wave: its MFMA phase and its softmax phase,
+    // each closed by a barrier.  Group 0's MFMA phase i is global phase 2i,
+    // group 1's is 2i + 1 (it opens with one extra barrier), so block i + 1
+    // is complete before the barrier that ends global phase 2i + 1.  Each
+    // group runs its own copy of the loop, with block 0 (no P V yet) peeled.
+    auto step = [&](int32_t i, auto first, auto group) __attribute__((always_inline)) {
+      mfma_phase(i, std::bool_constant<!decltype(first)::value>{}, std::true_type{});
+      if constexpr (decltype(group)::value == 0)
+        wait_vmcnt<63, true>();
+      else
+        wait_blocks(min(1, nkb - 2 - i));
+      block_barrier();
+      softmax_phase(i);
+      if constexpr (decltype(group)::value == 0)
+        wait_blocks(min(2, nkb - 2 - i));
+      else
+        wait_vmcnt<63, true>();
+      block_barrier();
+    };
+    auto run = [&](auto group) __attribute__((always_inline)) {
+      if constexpr (decltype(group)::value == 1) block_barrier();
+      step(0, std::true_type{}, group);
+      for (int32_t i = 1; i < nkb; ++i) step(i, std::false_type{}, group);
+      mfma_phase(nkb, std::true_type{}, std::false_type{});
+      if constexpr (decltype(group)::value == 0) block_barrier();
+    };
+
+    // block 0 (and the Q fragments) before the first phase
+    wait_blocks(min(2, nkb - 1));
+    block_barrier();
+    if (grp == 0)
+      run(std::integral_constant<int, 0>{});
+    else
+      run(std::integral_constant<int, 1>{});
+
+    // normalise and store: register r of o[db] is
+    // O[row li][db*32 + 8(r>>2) + 4 lg + (r&3)]
     Out* Oh = (Out*)a.O + b * a.so + q0 * a.ldo;
     const __amdgpu_buffer_rsrc_t ro = store_rsrc(Oh, ((rows_q - 1) * a.ldo + D) * (int64_t)sizeof(Out));
+    const float lt = l + __shfl_xor(l, 32);
+    const float inv = 1.f / lt;
+    const uint32_t rowoff = (uint32_t)((wave * 32 + li) * a.ldo * (int64_t)sizeof(Out));
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float lt = l[rb] + __shfl_xor(l[rb], 32);
-      const float inv = 1.f / lt;
-      const uint32_t rowoff = (uint32_t)((wave * WR + rb * 32 + li) * a.ldo * (int64_t)sizeof(Out));
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint32_t off = rowoff + (uint32_t)(db * 32 + 8 * g + 4 * lg) * (uint32_t)sizeof(Out);
-          const float v0 = o[rb][db][4 * g] * inv, v1 = o[rb][db][4 * g + 1] * inv;
-          const float v2 = o[rb][db][4 * g + 2] * inv, v3 = o[rb][db][4 * g + 3] * inv;
-          if constexpr (sizeof(Out) == 4)
-            buf_store16(ro, off, __builtin_bit_cast(u32x4, f32x4{v0, v1, v2, v3}));
-          else
-            buf_store8(ro, off, u32x2{pack2<Out>(v0, v1), pack2<Out>(v2, v3)});
-        }
-    }
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t off = rowoff + (uint32_t)(db * 32 + 8 * g + 4 * lg) * (uint32_t)sizeof(Out);
+        const float v0 = o[db][4 * g] * inv, v1 = o[db][4 * g + 1] * inv;
+        const float v2 = o[db][4 * g + 2] * inv, v3 = o[db][4 * g + 3] * inv;
+        if constexpr (sizeof(Out) == 4)
+          buf_store16(ro, off, __builtin_bit_cast(u32x4, f32x4{v0, v1, v2, v3}));
+        else
+          buf_store8(ro, off, u32x2{pack2<Out>(v0, v1), pack2<Out>(v2, v3)});
+      }
 
-    // every wave is done with the ring before the next item refills it
+    // every wave is done with the rings before the next item refills them
     if (w0 + gridDim.x < total) {
       wait_vmcnt<0>();
       block_barrier();
@@ -303,3 +366,4 @@ attn_fwd_kernel(AttnArgs a) {
 }
 
 }  // namespace tg
+

@@ -47,7 +47,7 @@ FAMILIES = {
               "generic_gemm_kernel"),
              lambda f: _gemm_source(f)),
     "group": (("group_gemm_kernel",), lambda f: _gemm_source(f)),
-    "attention": (("attn_fwd_kernel",),
+    "attention": (("attn_pp_kernel",),
                   lambda f: os.path.basename(f) in ("attention.hpp", "attention.hip", "tile_gemm.hpp",
                                                     "common.hpp")),
 }
