@@ -85,6 +85,15 @@ typedef enum {
  * planned on this entry to the 128 x 128 tile kernel (entry 4). */
 #define TG_TILE_PANEL 10
 
+/* Entry of the TG_VARIANT_TILE table served by the K-slice kernel, for small
+ * products with at most one 64 x 64 tile per CU ("Triton Optimization
+ * Reference", section 7: split-K for tiles too few to fill the machine).  The
+ * four waves of a work-group each walk a quarter of the tile's K steps (32
+ * deep) through a four-stage LDS ring of their own, then sum their partial
+ * tiles through LDS; lds_bytes = 4 * stages * (bm*bk + bk*bn) * 2.  Every
+ * transpose, epilogue and K (K = 0 included) is served. */
+#define TG_TILE_KSLICE 12
+
 /* plan.flags bits */
 #define TG_FLAG_EVEN_K 0x1 /* K is a multiple of the K-tile: no masked K step */
 #define TG_FLAG_VEC16 0x2  /* leading dims and contiguous extents allow 16-byte loads */

@@ -26,6 +26,7 @@ TG_OK, TG_ERR_INVALID, TG_ERR_UNSUPPORTED, TG_ERR_HIP, TG_ERR_TOO_LARGE = 0, 1, 
 VARIANT_GENERIC, VARIANT_TILE, VARIANT_SKINNY = 0, 1, 2
 TILE_PINGPONG, TILE_PINGPONG_EPI = 8, 9  # TG_TILE_PINGPONG, TG_TILE_PINGPONG_EPI
 TILE_PANEL = 10  # TG_TILE_PANEL
+TILE_KSLICE = 12  # TG_TILE_KSLICE
 SPLITK_MAX = 32  # TG_SPLITK_MAX
 SPLITK_SCRATCH_BYTES = 64 << 20  # TG_SPLITK_SCRATCH_BYTES
 FLAG_EVEN_K, FLAG_VEC16, FLAG_ROTATE_K, FLAG_PERSIST, FLAG_PREFETCH, FLAG_STREAM_C = 0x1, 0x2, 0x4, 0x8, 0x10, 0x20

@@ -10,6 +10,7 @@
 #include "tile_gemm.hpp"
 #include "pingpong_gemm.hpp"
 #include "panel_gemm.hpp"
+#include "kslice_gemm.hpp"
 #include "generic_gemm.hpp"
 
 
@@ -27,6 +28,8 @@ constexpr KernelFn tile_k() {
     return &panel_gemm_kernel<TG_IN, TG_OUT, TG_TB != 0>;
   else if constexpr (s.kind == kPanel)
     return nullptr;  // A stored K x M: the launcher sends these to a tile kernel
+  else if constexpr (s.kind == kKSlice)
+    return &kslice_gemm_kernel<TG_IN, TG_OUT, TG_TA != 0, TG_TB != 0, s.stages>;
   else
     return &tile_gemm_kernel<TG_IN, TG_OUT, s.bm, s.bn, s.bk, s.wm, s.wn, s.stages, s.occ,
                              s.dw ? s.dw : s.wm * s.wn, TG_TA != 0, TG_TB != 0>;

@@ -130,9 +130,12 @@ int choose_tile(const gemm_plan_t& p, int64_t batch) {
   // MFMA-bound with more than 128 of them: still 128x128 (1536^2 x 8192: 86
   // vs 97 us on 64x64 tiles; at 128 items, 1024x2048x8192, 64x64 wins 61 vs 87)
   if (mfma_bound && items(tg::kHbmTile) > 128) return tg::kMfmaMidTile;
-  // 64x64: with a long K the 4-deep ring keeps three steps' copies in flight
-  // (1000^3: 12.3 -> 11.1 us); with a short one the 2-deep ring's shorter
-  // prologue wins (256^3: 5.5 vs 5.9 us)
+  // 64x64 tiles, at most one per CU: the four waves of a tile split its K
+  // range (1000^3: 11.0 -> 10.4 us NN, 11.2 -> 9.7 us TN; 256^3: 5.5 -> 5.2 us)
+  if (items(tg::kSmallTile) <= 256 && k >= 128) return tg::kKSliceTile;
+  // more 64x64 tiles: with a long K the 4-deep ring keeps three steps'
+  // copies in flight (1000^3: 12.3 -> 11.1 us); with a short one the 2-deep
+  // ring's shorter prologue wins (256^3: 5.5 vs 5.9 us)
   return k >= 512 ? tg::kDeepSmallTile : tg::kSmallTile;
 }
 

@@ -14,7 +14,8 @@ enum TileKind {
   kTileKernel = 0,  // tile_gemm_kernel (tile_gemm.hpp)
   kPingPong = 1,    // pingpong_gemm_kernel without epilogue: persistent when there is enough work
   kPingPongEpi = 2,  // pingpong_gemm_kernel with the alpha/beta/bias epilogue (one tile per work-group)
-  kPanel = 3         // panel_gemm_kernel: short K, A resident in registers along a row panel of C
+  kPanel = 3,        // panel_gemm_kernel: short K, A resident in registers along a row panel of C
+  kKSlice = 4        // kslice_gemm_kernel: 64x64 tiles whose four waves split K (short chains)
 };
 
 struct TileShape {
@@ -50,8 +51,13 @@ constexpr TileShape kTiles[] = {
     // long K: with a K step's MFMAs far shorter than a copy's round trip, the
     // time per step is the round trip divided by the steps in flight
     {64, 64, 64, 2, 2, 4, 2},  // 11: 4-deep ring, 64 KiB
+    // 64x64 tiles whose four waves each walk a quarter of K through a ring
+    // of their own (kslice_gemm.hpp): 32-deep steps, four stages per wave
+    // (a fifth measured slower: 1000^3 10.4 -> 11.0 us)
+    {64, 64, 32, 2, 2, 4, 1, 0, kKSlice},  // 12: 4 x 32 KiB
 };
 constexpr int kSmallTile = 0, kMfmaMidTile = 1, kThinTile = 2, kWideTile = 3, kHbmTile = 4, kDeepSmallTile = 11;
+constexpr int kKSliceTile = 12;
 constexpr int kPingPongTile = 8, kPingPongEpiTile = 9, kPanelTile = 10;
 constexpr int kPanelKMax = kTiles[kPanelTile].bk;  // the panel kernel holds all of K at once
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
@@ -70,7 +76,8 @@ constexpr TileShape kGenericTiles[] = {
 constexpr int kNumGeneric = sizeof(kGenericTiles) / sizeof(kGenericTiles[0]);
 
 constexpr int lds_bytes_of(const TileShape& t) {
-  return t.kind == kPanel ? t.stages * t.bk * t.bn * 2
+  return t.kind == kPanel    ? t.stages * t.bk * t.bn * 2
+         : t.kind == kKSlice ? t.wm * t.wn * t.stages * (t.bm * t.bk + t.bk * t.bn) * 2
          : t.kind != kTileKernel ? (3 * t.bm * t.bk + 2 * t.bk * t.bn) * 2
                                  : t.stages * (t.bm * t.bk + t.bk * t.bn) * 2;
 }

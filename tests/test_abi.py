@@ -147,13 +147,13 @@ def test_plan_choices_for_the_workloads():
     p = tg.plan(256, 256, 256)
     assert (p.variant, p.bm, p.bn, p.flags & tg.FLAG_EVEN_K, p.flags & tg.FLAG_VEC16) == (
         tg.VARIANT_TILE, 64, 64, tg.FLAG_EVEN_K, tg.FLAG_VEC16)
-    assert (p.tile, p.stages) == (0, 2)  # short K: the 2-deep ring
+    assert (p.tile, p.stages) == (12, 4)  # 16 tiles: their four waves split K
     # 1000^3, every transpose: vector path (1000 = 8*125), ragged K tail
     for ta in (0, 1):
         for tb in (0, 1):
             p = tg.plan(1000, 1000, 1000, trans_a=ta, trans_b=tb)
             assert p.variant == tg.VARIANT_TILE and p.flags & tg.FLAG_VEC16 and not p.flags & tg.FLAG_EVEN_K
-            assert (p.tile, p.bm, p.bn, p.stages) == (11, 64, 64, 4)  # small, long K: the 4-deep 64x64 ring
+            assert (p.tile, p.bm, p.bn, p.stages) == (12, 64, 64, 4)  # 256 tiles, one per CU: K split 4 ways
             assert p.tiles_m * p.tiles_n >= 64
     # skinny M = 16, B stored N x K
     import torch
@@ -214,6 +214,9 @@ def test_lds_budget_matches_the_staging_formula_and_fits():
         elif p.variant == tg.VARIANT_TILE and p.tile == tg.TILE_PANEL:
             # two B buffers holding all of K
             assert p.lds_bytes == 2 * p.bk * p.bn * 2
+        elif p.variant == tg.VARIANT_TILE and p.tile == tg.TILE_KSLICE:
+            # a ring of its own for each of the four waves
+            assert p.lds_bytes == 4 * roofline.lds_budget(p.bm, p.bn, p.bk, p.stages)
         elif p.variant != tg.VARIANT_SKINNY:
             assert p.lds_bytes == roofline.lds_budget(p.bm, p.bn, p.bk, p.stages)
         assert p.lds_bytes <= roofline.MI355X_LDS_PER_WORKGROUP
@@ -352,6 +355,7 @@ def test_python_constants_match_the_header():
     assert int(defs["TG_TILE_PINGPONG"], 0) == tg.TILE_PINGPONG
     assert int(defs["TG_TILE_PINGPONG_EPI"], 0) == tg.TILE_PINGPONG_EPI
     assert int(defs["TG_TILE_PANEL"], 0) == tg.TILE_PANEL
+    assert int(defs["TG_TILE_KSLICE"], 0) == tg.TILE_KSLICE
     assert int(defs["TG_SPLITK_MAX"], 0) == tg.SPLITK_MAX
     m = re.search(r"#define\s+TG_SPLITK_SCRATCH_BYTES\s+\((\d+)ull << (\d+)\)", text)
     assert int(m.group(1)) << int(m.group(2)) == tg.SPLITK_SCRATCH_BYTES
