@@ -234,6 +234,7 @@ def main():
         "pct_hbm_peak": round(100 * nbytes / (ms_per_step / 1e3) / PEAK_HBM, 2),
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": runit,
                      "frac": round(achieved / peak, 4), "traffic": profiling.read_traffic(p.name),
+                     "traffic_source": profiling.traffic_note(p.name),
                      "kernel_ms": round(kernel_s * 1e3, 5),
                      "kernel_ms_each_min": round(float(np.min(kms)), 5),
                      "kernel_ms_each_p90": round(float(np.percentile(kms, 90)), 5),
@@ -398,7 +399,7 @@ def run_configs(torch, tg, profiling):
                 "bound": bound, "frac": round(rate / peak, 4),
                 "operand_copies": copies, "hot_cache": small, "launches": steps, "queued_ahead": bool(ahead),
                 "tile_index": int(pl.tile), "variant": int(pl.variant),
-                "traffic": profiling.read_traffic(p.name),
+                "traffic": profiling.read_traffic(p.name), "traffic_source": profiling.traffic_note(p.name),
                 "algorithmic": {"flops": flops, "bytes": nbytes}}
             del As, Bs, C, A0, B0
             torch.cuda.empty_cache()
@@ -501,6 +502,7 @@ def run_attention(args, torch, tg, profiling):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA / 1e12,
                      "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_MFMA, 4),
                      "traffic": profiling.read_traffic(p.name),
+                     "traffic_source": profiling.traffic_note(p.name),
                      "kernel_ms": round(kernel_s * 1e3, 5),
                      "kernel_ms_each_min": round(float(np.min(kms)), 5),
                      "kernel_ms_each_p90": round(float(np.percentile(kms, 90)), 5),
@@ -603,6 +605,7 @@ def run_group(args, torch, tg, profiling):
                               "grouped_speedup": round(sep_ms / mean_ms, 3)},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": runit,
                      "frac": round(achieved / peak, 4), "traffic": profiling.read_traffic(p.name),
+                     "traffic_source": profiling.traffic_note(p.name),
                      "kernel_ms": round(kernel_s * 1e3, 5),
                      "kernel_ms_each_min": round(float(np.min(kms)), 5),
                      "kernel_ms_each_p90": round(float(np.percentile(kms, 90)), 5),

@@ -44,7 +44,7 @@ def _gemm_source(f: str) -> bool:
 # kernel families: the kernels' name patterns and the sources they are built from
 FAMILIES = {
     "gemm": (("tile_gemm_kernel", "pingpong_gemm_kernel", "panel_gemm_kernel", "skinny_gemm_kernel",
-              "generic_gemm_kernel"),
+              "kslice_gemm_kernel", "generic_gemm_kernel"),
              lambda f: _gemm_source(f)),
     "group": (("group_gemm_kernel",), lambda f: _gemm_source(f)),
     "attention": (("attn_pp_kernel",),
@@ -138,6 +138,14 @@ def traffic(out_dir: str, workload: str) -> str:
         f"traffic_bytes = {fetch + write:.0f}",
     ]
     return "\n".join(lines)
+
+
+def traffic_note(workload: str) -> str:
+    """Where a bench record's `traffic` comes from (it is never measured in the timed run)."""
+    if read_traffic(workload) is None:
+        return f"null: profiles/{workload}_traffic.txt is missing or was taken on other kernel sources"
+    return (f"profiles/{workload}_traffic.txt: FETCH_SIZE and WRITE_SIZE counter runs of the same kernel "
+            "sources (source hash matched), scaled by a plain-copy calibration; not measured in this run")
 
 
 def read_traffic(workload: str):
