@@ -32,7 +32,7 @@ constexpr KernelFn tile_k() {
     return &kslice_gemm_kernel<TG_IN, TG_OUT, TG_TA != 0, TG_TB != 0, s.stages>;
   else
     return &tile_gemm_kernel<TG_IN, TG_OUT, s.bm, s.bn, s.bk, s.wm, s.wn, s.stages, s.occ,
-                             s.dw ? s.dw : s.wm * s.wn, TG_TA != 0, TG_TB != 0>;
+                             s.dw ? s.dw : s.wm * s.wn, TG_TA != 0, TG_TB != 0, s.kind == kTileEpi>;
 }
 template <int T>
 constexpr KernelFn generic_k() {

@@ -386,6 +386,9 @@ static tg_status launch(const gemm_plan_t* plan, const gemm_epilogue_t* epi, int
   }
   // The panel kernel; what it does not serve goes to the 128 x 128 tile.
   if (variant == TG_VARIANT_TILE && kTiles[tile].kind == tg::kPanel && (a.epi || !panel_ok(p))) tile = tg::kHbmTile;
+  // The tile kernel's entries leave the epilogue out; a call with one goes
+  // to the entry of the same shape class that has it compiled in.
+  if (variant == TG_VARIANT_TILE && a.epi && kTiles[tile].kind == tg::kTileKernel) tile = tg::epi_twin(tile);
   a.span = 0;
   // Tile kernel: an operand that only one tile of the launch reads -- A when
   // there is one column of tiles, B when there is one row, and neither when
@@ -393,7 +396,7 @@ static tg_status launch(const gemm_plan_t* plan, const gemm_epilogue_t* epi, int
   // L2 with non-temporal loads (measured 8% faster on O = P V, whose P rows
   // otherwise evict the V panel the 16 row blocks of a head share).
   a.nt_ab = 0;
-  if (variant == TG_VARIANT_TILE && kTiles[tile].kind == tg::kTileKernel) {
+  if (variant == TG_VARIANT_TILE && (kTiles[tile].kind == tg::kTileKernel || kTiles[tile].kind == tg::kTileEpi)) {
     const int64_t tm = cdiv(p.m, kTiles[tile].bm), tn = cdiv(p.n, kTiles[tile].bn);
     if (tn == 1 && (batch == 1 || sA != 0)) a.nt_ab |= 1;
     if (tm == 1 && (batch == 1 || sB != 0)) a.nt_ab |= 2;

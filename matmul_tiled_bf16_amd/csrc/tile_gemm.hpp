@@ -434,9 +434,14 @@ struct Frags {
 
 // The kernel body.  KA is GemmArgs (one problem, or a batch of equal
 // shapes) or, with GROUP, GroupArgs (a table of problems, each item looks its
-// problem up; persistent modes and K rotation are off).
+// problem up; persistent modes and K rotation are off).  EPI compiles in the
+// alpha/beta/bias epilogue; without it args.epi is ignored (the launcher
+// sends epilogue calls to EPI entries), and the register allocator does not
+// have to make room for the epilogue's C reads -- with them the HBM-bound
+// 128 x 128 tile spilled, and its spill reloads, which wait for every copy
+// in flight, slowed O = P V by 6-15%.
 template <typename In, typename Out, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int DW, bool TA,
-          bool TB, bool GROUP, typename KA>
+          bool TB, bool GROUP, bool EPI, typename KA>
 __device__ __forceinline__ void tile_gemm_body(const KA& kargs) {
   const GemmArgs& args = [&]() -> const GemmArgs& {
     if constexpr (GROUP) return kargs.g;
@@ -547,7 +552,7 @@ __device__ __forceinline__ void tile_gemm_body(const KA& kargs) {
   // stores, a fixed count per wave -- stay outstanding.
   constexpr int ST = FM * FN * 4;  // store instructions of store_tile_vec
   constexpr bool PERSIST_OK = (D - 1) * PER_STEP + ST < 64;  // fits the counter
-  const bool persist = !GROUP && PERSIST_OK && args.persist == 1 && !args.epi;
+  const bool persist = !GROUP && PERSIST_OK && args.persist == 1 && !(EPI && args.epi);
   // the item being computed: matrix, tile origin, walk rotation, and the
   // source pointers / remaining bytes / K - k0 of the next step to load
   int64_t b = 0, m0 = 0, n0 = 0, rot = 0;
@@ -810,7 +815,7 @@ __device__ __forceinline__ void tile_gemm_body(const KA& kargs) {
       for (; kt < nk; ++kt) stage_dyn(kt);
     }
 
-    if (!GROUP && args.epi) {
+    if (!GROUP && EPI && args.epi) {
       const char* Cb = (const char*)Cp + b * args.sC * (int64_t)sizeof(Out);
       const int64_t r0 = m0 + wm0, c0 = n0 + wn0;
       if (N % 4 == 0 || n0 + BN <= N) {  // 4-column groups never straddle column N
@@ -889,14 +894,15 @@ __device__ __forceinline__ void tile_gemm_body(const KA& kargs) {
   }
 }
 
-template <typename In, typename Out, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int DW, bool TA, bool TB>
+template <typename In, typename Out, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int DW, bool TA, bool TB,
+          bool EPI>
 __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) tile_gemm_kernel(GemmArgs args) {
-  tile_gemm_body<In, Out, BM, BN, BK, WM, WN, STAGES, OCC, DW, TA, TB, false>(args);
+  tile_gemm_body<In, Out, BM, BN, BK, WM, WN, STAGES, OCC, DW, TA, TB, false, EPI>(args);
 }
 
 template <typename In, typename Out, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int DW, bool TA, bool TB>
 __global__ void __launch_bounds__(WM * WN * 64, OCC * WM * WN / 4) group_gemm_kernel(GroupArgs args) {
-  tile_gemm_body<In, Out, BM, BN, BK, WM, WN, STAGES, OCC, DW, TA, TB, true>(args);
+  tile_gemm_body<In, Out, BM, BN, BK, WM, WN, STAGES, OCC, DW, TA, TB, true, false>(args);
 }
 
 }  // namespace tg

@@ -15,7 +15,8 @@ enum TileKind {
   kPingPong = 1,    // pingpong_gemm_kernel without epilogue: persistent when there is enough work
   kPingPongEpi = 2,  // pingpong_gemm_kernel with the alpha/beta/bias epilogue (one tile per work-group)
   kPanel = 3,        // panel_gemm_kernel: short K, A resident in registers along a row panel of C
-  kKSlice = 4        // kslice_gemm_kernel: 64x64 tiles whose four waves split K (short chains)
+  kKSlice = 4,       // kslice_gemm_kernel: 64x64 tiles whose four waves split K (short chains)
+  kTileEpi = 5       // tile_gemm_kernel with the alpha/beta/bias epilogue compiled in
 };
 
 struct TileShape {
@@ -55,9 +56,20 @@ constexpr TileShape kTiles[] = {
     // of their own (kslice_gemm.hpp): 32-deep steps, four stages per wave
     // (a fifth measured slower: 1000^3 10.4 -> 11.0 us)
     {64, 64, 32, 2, 2, 4, 1, 0, kKSlice},  // 12: 4 x 32 KiB
+    // the tile kernel with the epilogue compiled in: the launcher sends a call
+    // with an epilogue planned on a tile-kernel entry to the twin of its
+    // shape class (the other entries leave the epilogue's registers free)
+    {64, 64, 64, 2, 2, 2, 1, 0, kTileEpi},      // 13: twin of 0, 2, 11
+    {128, 128, 64, 2, 2, 2, 1, 0, kTileEpi},    // 14: twin of 1, 5, 6, 7
+    {256, 256, 32, 2, 4, 4, 1, 0, kTileEpi},    // 15: twin of 3
+    {128, 128, 64, 2, 2, 2, 2, 0, kTileEpi},    // 16: twin of 4
 };
 constexpr int kSmallTile = 0, kMfmaMidTile = 1, kThinTile = 2, kWideTile = 3, kHbmTile = 4, kDeepSmallTile = 11;
 constexpr int kKSliceTile = 12;
+// the epilogue twin of a tile-kernel entry
+constexpr int epi_twin(int t) {
+  return t == 3 ? 15 : t == 4 ? 16 : (t == 1 || t == 5 || t == 6 || t == 7) ? 14 : 13;
+}
 constexpr int kPingPongTile = 8, kPingPongEpiTile = 9, kPanelTile = 10;
 constexpr int kPanelKMax = kTiles[kPanelTile].bk;  // the panel kernel holds all of K at once
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
@@ -78,8 +90,8 @@ constexpr int kNumGeneric = sizeof(kGenericTiles) / sizeof(kGenericTiles[0]);
 constexpr int lds_bytes_of(const TileShape& t) {
   return t.kind == kPanel    ? t.stages * t.bk * t.bn * 2
          : t.kind == kKSlice ? t.wm * t.wn * t.stages * (t.bm * t.bk + t.bk * t.bn) * 2
-         : t.kind != kTileKernel ? (3 * t.bm * t.bk + 2 * t.bk * t.bn) * 2
-                                 : t.stages * (t.bm * t.bk + t.bk * t.bn) * 2;
+         : (t.kind == kPingPong || t.kind == kPingPongEpi) ? (3 * t.bm * t.bk + 2 * t.bk * t.bn) * 2
+                                                           : t.stages * (t.bm * t.bk + t.bk * t.bn) * 2;
 }
 
 // Whether the tile kernel can run persistently: the first wait of a
@@ -87,7 +99,7 @@ constexpr int lds_bytes_of(const TileShape& t) {
 // one plus the item's store instructions, and that count must fit the 6-bit
 // vector-memory counter.
 constexpr bool persist_ok(const TileShape& t) {
-  if (t.kind != kTileKernel) return false;
+  if (t.kind != kTileKernel && t.kind != kTileEpi) return false;
   const int copy_waves = t.dw ? t.dw : t.wm * t.wn;
   const int per_step = (t.bm * t.bk * 2 / 1024) / copy_waves + (t.bk * t.bn * 2 / 1024) / copy_waves;
   const int d = t.stages >= 3 ? t.stages - 1 : t.stages;
