@@ -74,8 +74,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="square_8192")
     ap.add_argument("--rotate", type=int, default=0,
-                    help="copies of B to cycle through (defeats the 256 MiB Infinity Cache); "
-                         "default 4 for HBM-bound workloads, 1 otherwise")
+                    help="copies of the larger operand to cycle through (defeats the 256 MiB Infinity "
+                         "Cache); default 4 for HBM-bound workloads, 1 otherwise")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile", type=int, default=None, help="override the planner's tile (same variant)")
     ap.add_argument("--no-persist", action="store_true", help="clear the plan's persistent-launch flags")
@@ -140,8 +140,11 @@ def main():
     bound = roofline.bound(p.m, p.n, p.k, 2, out_size, p.batch, PEAK_MFMA, PEAK_HBM)
     rotate = args.rotate or (4 if bound == "hbm" else 1)
 
-    A = up(p.A)
-    Bs = [up(p.B)] + [up(p.B).clone() for _ in range(rotate - 1)]
+    # the copies cycle through the operand that dominates the bytes (P of
+    # O = P V is 16x its V), so that no launch finds it in the Infinity Cache
+    big_a = p.A.size > p.B.size
+    As = [up(p.A)] + ([up(p.A).clone() for _ in range(rotate - 1)] if big_a else [])
+    Bs = [up(p.B)] + ([up(p.B).clone() for _ in range(rotate - 1)] if not big_a else [])
     Cs = [torch.empty((p.batch, p.m, p.n) if p.batch > 1 else (p.m, p.n), dtype=tout, device=dev)
           for _ in range(min(rotate, 2))]
     stream = torch.cuda.current_stream()
@@ -167,6 +170,7 @@ def main():
             pl.flags &= ~tg.FLAG_STREAM_C
         elif args.stream_c == 1:
             pl.flags |= tg.FLAG_STREAM_C
+        A = As[i % len(As)]
         B = Bs[i % len(Bs)]
         C = Cs[i % len(Cs)]
         if epi:
@@ -225,7 +229,7 @@ def main():
         "dtype": "bf16" if p.in_dtype == "bf16" else "fp16",
         "data": "synthetic",
         "config": {"workload": p.name, "m": p.m, "n": p.n, "k": p.k, "batch": p.batch, "op": trans,
-                   "in_dtype": p.in_dtype, "out_dtype": p.out_dtype, "b_copies": len(Bs),
+                   "in_dtype": p.in_dtype, "out_dtype": p.out_dtype, "a_copies": len(As), "b_copies": len(Bs),
                    "variant": int(pl.variant), "tile_index": int(pl.tile), "plan_flags": int(pl.flags),
                    **({"epilogue": {"alpha": args.alpha, "beta": args.beta, "bias": bool(args.bias)}} if epi else {})},
         "tflops": round(tflops, 2),
