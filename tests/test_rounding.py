@@ -127,7 +127,7 @@ def test_tile_kernels(dtype):
     # then 8192 ties and neighbours of ties
     p = run(dtype, 544, 256)
     assert p.variant == tg.VARIANT_TILE
-    for tile in (0, 1, 4, 11):
+    for tile in (0, 1, 4, 11, tg.TILE_KSLICE):
         run(dtype, 544, 256, variant=tg.VARIANT_TILE, tile=tile)
 
 
