@@ -136,6 +136,22 @@ def test_every_tile_gives_the_same_answer():
                   f"variant={variant} tile={tile}")
 
 
+@pytest.mark.parametrize("ta,tb", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_kslice_uneven_k_splits(ta, tb):
+    """The K-slice kernel gives wave w the K steps [w nk / 4, (w + 1) nk / 4):
+    with one to three steps some waves get none, and a ragged last step is
+    zero-filled; M and N end inside a tile.  Integer data with NaN padding:
+    bit for bit, nothing written outside C.  (The kernel reads 16-byte units:
+    extents and leading dimensions are multiples of 8.)"""
+    cases = [(64, 64, 8), (72, 40, 16), (64, 200, 40), (136, 64, 96), (104, 96, 136), (256, 136, 200)]
+    for i, (m, n, k) in enumerate(cases):
+        pad = (8, 16, 8) if i % 2 else (0, 0, 0)
+        got, ref, A, B, pl, _ = run_case(m, n, k, ta, tb, "fp32", pad=pad, seed=50 + i, dist=("int", -8, 8),
+                                         variant=tg.VARIANT_TILE, tile=tg.TILE_KSLICE)
+        assert pl.tile == tg.TILE_KSLICE
+        check_exact(got, ref, "fp32", f"kslice m={m} n={n} k={k} ta={ta} tb={tb} pad={pad}")
+
+
 def test_skinny_variants_and_tails():
     assert tg.variant_tiles(tg.VARIANT_SKINNY) == 2
     cases = [(0, 16), (0, 5), (1, 32), (1, 17)]
