@@ -259,7 +259,7 @@ def clock_during(torch, stream, step, kernel_s, seconds=3.0):
     back-to-back launches of the timed step (the timed region itself is too
     short to sample; this window runs the same launches right after it).
 
-    The driver's metrics table (amdsmi_get_gpu_metrics_info) refreshes only a
+    The GPU metrics table (amdsmi_get_gpu_metrics_info) refreshes only a
     few times a second, so every poll inside the window is not a new reading:
     only refreshes first seen after the clock settled (0.3 s in) and before
     the GPU went idle count, one sample per distinct firmware timestamp.
@@ -269,7 +269,7 @@ def clock_during(torch, stream, step, kernel_s, seconds=3.0):
     try:
         import amdsmi
         amdsmi.amdsmi_init()
-    except Exception as e:  # no amdsmi library or no driver access
+    except Exception as e:  # no amdsmi library or no access to the device
         return {"error": f"amdsmi unavailable: {type(e).__name__}"}
     try:
         handles = amdsmi.amdsmi_get_processor_handles()
