@@ -112,3 +112,39 @@ def test_group_matches_single_launches_on_integers():
         torch.cuda.synchronize()
         assert torch.equal(Cg, Cs), (m, n, k)
         assert A.dtype == tin
+
+
+def test_grouped_moe_workload_sampled():
+    """The grouped-launch workload at its full size (32 ragged experts over
+    8192 token rows, K = N = 1024, bf16 out), launched as the benchmark does
+    -- one table whose problems are row ranges of X and Y -- and checked on a
+    sample of each expert's outputs (tile edges included) against the oracle.
+    Rows outside every expert's range keep their canary."""
+    p = synth.grouped_moe()
+    T = int(p.counts.sum())
+    off = p.offsets
+    Xg, Wg = to_gpu(p.X), to_gpu(p.W)
+    Y = torch.full((T + 8, p.n), CANARY, dtype=torch.bfloat16, device="cuda")
+    probs = []
+    for e, c in enumerate(p.counts):
+        c = int(c)
+        probs.append((c, p.n, p.k, p.k, p.n, p.n, Xg[int(off[e]):int(off[e]) + c], Wg[e],
+                      Y[int(off[e]):int(off[e]) + c]))
+    tg.gemm_group_run(tg.TG_BF16, tg.TG_BF16, False, False, probs)
+    torch.cuda.synchronize()
+    got_all = values(Y)
+    assert np.all(got_all[T:] == CANARY), "wrote past the last expert's rows"
+    rng = np.random.default_rng(77)
+    t = tol_fp32(p.k, oracle.max_abs(p.X), oracle.max_abs(p.W))
+    for e, c in enumerate(p.counts):
+        c = int(c)
+        if c == 0:
+            continue
+        rows = np.unique(np.concatenate([rng.integers(0, c, 96), [0, c - 1, min(c - 1, 127), min(c - 1, 128)]]))
+        cols = rng.integers(0, p.n, rows.size)
+        cols[:2] = [0, p.n - 1]
+        idx = np.stack([np.zeros_like(rows), rows, cols], axis=1)
+        X_e = np.ascontiguousarray(p.X[int(off[e]):int(off[e]) + c])
+        ref = oracle.gemm(X_e, p.W[e], m=c, n=p.n, k=p.k, idx=idx)
+        got = got_all[int(off[e]) + rows, cols]
+        check(got, ref, t, "bf16", f"expert {e} ({c} rows)")
