@@ -537,10 +537,16 @@ __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(GemmArgs args) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers
       }
       barrier();
+      // the MFMA phase at a raised wave priority: when both waves of a SIMD
+      // have an instruction ready, the MFMA goes first (measured 0.6-0.7%
+      // faster on 8192^3, two boxes; raising the memory phase instead gained
+      // nothing)
+      __builtin_amdgcn_s_setprio(2);
       if (kk == 0)
         comp(std::true_type{});
       else
         comp(std::false_type{});
+      __builtin_amdgcn_s_setprio(0);
       if constexpr (G == 0) {
         if (copied) {
           // B(g + 1) has landed; the stores issued after it may not have
