@@ -120,16 +120,22 @@ int choose_tile(const gemm_plan_t& p, int64_t batch) {
   const double flops = 2.0 * (double)m * (double)n * (double)k;
   const double bytes = 2.0 * ((double)m * k + (double)k * n) + (double)out_size * m * n;
   const bool mfma_bound = bytes > 0 && flops / bytes > 312.5;
-  // 256x256, 8 waves: from 128 work items on (measured: 2048x4096x8192
-  // 0.172 vs 0.194 ms on 128x128 tiles, 4096^2x8192 0.204 vs 0.370 ms; at 64
-  // items, 2048^2x8192, the 128x128 tiles' 256 work-groups win)
-  if (mfma_bound && items(tg::kWideTile) >= 128 && k > 0) return tg::kPingPongTile;
+  // 256x256, 8 waves: from more than 128 work items on.  At exactly 128
+  // (half the CUs) the 128x128 tiles with two work-groups per CU, one round of
+  // 512, win at every K (8192x1024 and 2048x4096, K = 1024 .. 8192: 24 vs 31
+  // us .. 128 vs 140 us); from 144 items on the ping-pong kernel does (3072^2
+  // x 8192: 141 vs 196 us; 4096^2 x 8192: 0.204 vs 0.370 ms).
+  if (mfma_bound && items(tg::kWideTile) > 128 && k > 0) return tg::kPingPongTile;
   // short K and many tiles: runs along row panels, A held in registers
   if (!mfma_bound && panel_ok(p) && items(tg::kPanelTile) >= 2048) return tg::kPanelTile;
-  if (items(tg::kHbmTile) >= 256) return mfma_bound ? tg::kMfmaMidTile : tg::kHbmTile;  // 128x128
-  // MFMA-bound with more than 128 of them: still 128x128 (1536^2 x 8192: 86
-  // vs 97 us on 64x64 tiles; at 128 items, 1024x2048x8192, 64x64 wins 61 vs 87)
-  if (mfma_bound && items(tg::kHbmTile) > 128) return tg::kMfmaMidTile;
+  // 128x128, two work-groups per CU: HBM-bound products, and MFMA-bound ones
+  // below the ping-pong kernel's range (measured faster than one work-group
+  // per CU on every such shape tried: 1536x3072x8192 105 vs 173 us, 2560^2 x
+  // 8192 117 vs 176 us, 2048^2 x 8192 88 vs 95 us)
+  if (items(tg::kHbmTile) >= 256) return tg::kHbmTile;
+  // MFMA-bound with more than 128 of them: still 128x128 (1536^2 x 8192: 84
+  // vs 99 us on the 64x64 ring; at 128 items, 1024x2048x8192, 64x64 wins)
+  if (mfma_bound && items(tg::kHbmTile) > 128) return tg::kHbmTile;
   // 64x64 tiles, at most one per CU: the four waves of a tile split its K
   // range (1000^3: 11.0 -> 10.4 us NN, 11.2 -> 9.7 us TN; 256^3: 5.5 -> 5.2 us)
   if (items(tg::kSmallTile) <= 256 && k >= 128) return tg::kKSliceTile;

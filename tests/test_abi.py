@@ -186,11 +186,13 @@ def test_plan_choices_for_the_workloads():
         tg.plan(64, 64, 64, batch=0)
     p = tg.plan(8192, 8192, 8192, out_dtype=torch.bfloat16)
     assert (p.variant, p.bm, p.bn, p.wg_threads) == (tg.VARIANT_TILE, 256, 256, 512) and p.tiles_m * p.tiles_n == 1024
-    # MFMA-bound products take the ping-pong kernel from 128 of its 256 x 256 work items on
-    assert tg.plan(2048, 4096, 8192, out_dtype=torch.bfloat16).tile == tg.TILE_PINGPONG  # 128 items
+    # MFMA-bound products take the ping-pong kernel above 128 of its 256 x 256 work items,
+    # the 128 x 128 tile with two work-groups per CU below
+    assert tg.plan(3072, 3072, 8192, out_dtype=torch.bfloat16).tile == tg.TILE_PINGPONG  # 144 items
+    assert tg.plan(2048, 4096, 8192, out_dtype=torch.bfloat16).tile == 4                # 128 items
     assert tg.plan(1024, 1024, 4096, batch=16).tile == tg.TILE_PINGPONG                # 16 x 16 items
-    assert tg.plan(2048, 2048, 8192, out_dtype=torch.bfloat16).tile == 1                # 64 items: 128 x 128
-    assert tg.plan(1536, 1536, 8192, out_dtype=torch.bfloat16).tile == 1                # 144 128 x 128 items
+    assert tg.plan(2048, 2048, 8192, out_dtype=torch.bfloat16).tile == 4                # 64 items: 128 x 128
+    assert tg.plan(1536, 1536, 8192, out_dtype=torch.bfloat16).tile == 4                # 144 128 x 128 items
     assert tg.plan(1024, 2048, 8192, out_dtype=torch.bfloat16).tile == 11               # 128: the 64 x 64 ring
     assert p.flags & tg.FLAG_PERSIST and p.flags & tg.FLAG_PREFETCH  # MFMA-bound: prefetch during stores
     assert p.workspace_bytes == 0
