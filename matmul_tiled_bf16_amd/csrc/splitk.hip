@@ -10,7 +10,7 @@
 // part as one more product, and one reduction kernel adds the slices in a
 // fixed order (slice 0 first) and writes C in the output type.  The batched
 // product gets the planner's kernel for its shape -- the ping-pong kernel
-// once the parts make 128 or more of its 256x256 work items.  Every launch
+// once the parts make more than 128 of its 256x256 work items.  Every launch
 // goes on the caller's stream; the library allocates nothing.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
