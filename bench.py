@@ -5,8 +5,11 @@
 
 One step = plan + launch of the whole product for one set of synthetic inputs
 already resident in HBM (gemm_plan on the host, then gemm_run / bmm_run).
-W untimed steps, then exactly K timed steps between two device
-synchronisations.  Prints one JSON line.
+Before the W untimed warmup steps, the same step runs back to back for
+--settle seconds (0.3 by default; reported as "clock_settle"): after an idle
+GPU the first ~100 launches of a large product run 4-19% slower than the
+steady state while the clocks and the power controller settle.  Then exactly
+K timed steps between two device synchronisations.  Prints one JSON line.
 
 Workloads (seeded synthetic inputs from synth/):
   square_8192   8192^3, NN, bf16 in, bf16 out        (default; MFMA-bound)
@@ -88,6 +91,8 @@ def main():
     ap.add_argument("--beta", type=float, default=0.0, help="epilogue: scale of C's prior contents")
     ap.add_argument("--bias", action="store_true", help="epilogue: add a per-column bias")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of back-to-back steps before the warmup, while the clocks settle")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-configuration measurements added to the default run")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -185,6 +190,7 @@ def main():
             tg.bmm_run(pl, p.batch, p.stride_a, p.stride_b, p.stride_c, A, B, C, stream)
         return pl
 
+    settled = settle(torch, step, args.settle)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -202,7 +208,8 @@ def main():
     # same launches, queued while the stream is held by a GPU-side sleep, so
     # that host time between launches (plan, marshalling) cannot show up
     # between the events.
-    mean_ms, kms, queued_ahead = gated_kernel_ms(torch, stream, step, args.steps, max(args.warmup, 1))
+    warm = held_warm(settled, args.warmup)
+    mean_ms, kms, queued_ahead = gated_kernel_ms(torch, stream, step, args.steps, warm)
     kernel_s = mean_ms / 1e3
 
     tflops = flops / (ms_per_step / 1e3) / 1e12
@@ -222,6 +229,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": settled,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -243,6 +251,7 @@ def main():
                      "kernel_ms_each_min": round(float(np.min(kms)), 5),
                      "kernel_ms_each_p90": round(float(np.percentile(kms, 90)), 5),
                      "launches_queued_ahead": bool(queued_ahead),
+                     "launches_warm_before_events": held_warm(settled, args.warmup),
                      "algorithmic": {"flops": flops, "bytes": nbytes}},
     }
     line["clock"] = clock_during(torch, stream, step, kernel_s)
@@ -386,10 +395,8 @@ def run_configs(torch, tg, profiling):
                 else:
                     tg.bmm_run(pl, p.batch, p.stride_a, p.stride_b, p.stride_c, A, B, C, stream)
 
-            for i in range(5):
-                step(i)
-            torch.cuda.synchronize()
-            mean_ms, kms, ahead = gated_kernel_ms(torch, stream, step, steps, 5)
+            settled = settle(torch, step, 0.05)
+            mean_ms, kms, ahead = gated_kernel_ms(torch, stream, step, steps, held_warm(settled, 5))
             assert torch.isfinite(C.float()).all().item(), f"{p.name}: non-finite output"
             s = mean_ms / 1e3
             rate = flops / s / 1e12 if bound == "mfma" else nbytes / s / 1e9
@@ -470,6 +477,7 @@ def run_attention(args, torch, tg, profiling):
         tg.attention_fwd(tg.TG_BF16, tg.TG_FP32 if out_size == 4 else tg.TG_BF16, p.batch, p.n_q, p.n_k, d,
                          p.scale, Q, d, p.n_q * d, K, d, p.n_k * d, V, d, p.n_k * d, O, d, p.n_q * d, stream)
 
+    settled = settle(torch, step, args.settle)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -480,7 +488,7 @@ def run_attention(args, torch, tg, profiling):
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     assert torch.isfinite(Os[0].float()).all().item(), "non-finite output"
-    mean_ms, kms, queued_ahead = gated_kernel_ms(torch, stream, step, args.steps, max(args.warmup, 1))
+    mean_ms, kms, queued_ahead = gated_kernel_ms(torch, stream, step, args.steps, held_warm(settled, args.warmup))
     kernel_s = mean_ms / 1e3
     tflops = flops / (ms_per_step / 1e3) / 1e12
     achieved = flops / kernel_s / 1e12
@@ -491,6 +499,7 @@ def run_attention(args, torch, tg, profiling):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": settled,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -511,6 +520,7 @@ def run_attention(args, torch, tg, profiling):
                      "kernel_ms_each_min": round(float(np.min(kms)), 5),
                      "kernel_ms_each_p90": round(float(np.percentile(kms, 90)), 5),
                      "launches_queued_ahead": bool(queued_ahead),
+                     "launches_warm_before_events": held_warm(settled, args.warmup),
                      "algorithmic": {"flops": flops, "bytes": nbytes}},
     }
     if not args.no_cpu_baseline:
@@ -563,6 +573,7 @@ def run_group(args, torch, tg, profiling):
             pl = tg.plan(int(c), p.n, p.k, in_dtype=torch.bfloat16, out_dtype=torch.bfloat16)
             tg.gemm_run(pl, X[int(off[e]):int(off[e + 1])], W[e], Y[int(off[e]):int(off[e + 1])], stream)
 
+    settled = settle(torch, step, args.settle)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -572,8 +583,9 @@ def run_group(args, torch, tg, profiling):
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     assert torch.isfinite(Ys[0].float()).all().item(), "non-finite output"
-    mean_ms, kms, queued_ahead = gated_kernel_ms(torch, stream, step, args.steps, max(args.warmup, 1))
-    sep_ms, _, sep_ahead = gated_kernel_ms(torch, stream, step_separate, max(args.steps // 4, 3), 2)
+    mean_ms, kms, queued_ahead = gated_kernel_ms(torch, stream, step, args.steps, held_warm(settled, args.warmup))
+    sep_ms, _, sep_ahead = gated_kernel_ms(torch, stream, step_separate, max(args.steps // 4, 3),
+                                           held_warm(settle(torch, step_separate, 0.05), 2, cap=25))
     flops = p.flops
     nbytes = p.algorithmic_bytes(es)
     bound = "mfma" if flops / nbytes > PEAK_MFMA / PEAK_HBM else "hbm"
@@ -590,6 +602,7 @@ def run_group(args, torch, tg, profiling):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": settled,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -614,6 +627,7 @@ def run_group(args, torch, tg, profiling):
                      "kernel_ms_each_min": round(float(np.min(kms)), 5),
                      "kernel_ms_each_p90": round(float(np.percentile(kms, 90)), 5),
                      "launches_queued_ahead": bool(queued_ahead),
+                     "launches_warm_before_events": held_warm(settled, args.warmup),
                      "algorithmic": {"flops": flops, "bytes": nbytes}},
     }
     if not args.no_cpu_baseline:
@@ -650,6 +664,7 @@ def run_splitk(args, torch, tg, profiling):
     def step_plain(i):
         tg.gemm_run(pl, A, B, Cs[i % 2], stream)
 
+    settled = settle(torch, step, args.settle)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -659,8 +674,9 @@ def run_splitk(args, torch, tg, profiling):
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     assert torch.isfinite(Cs[0].float()).all().item(), "non-finite output"
-    mean_ms, kms, queued_ahead = gated_kernel_ms(torch, stream, step, args.steps, max(args.warmup, 1))
-    plain_ms, _, plain_ahead = gated_kernel_ms(torch, stream, step_plain, max(args.steps // 2, 3), 2)
+    mean_ms, kms, queued_ahead = gated_kernel_ms(torch, stream, step, args.steps, held_warm(settled, args.warmup))
+    plain_ms, _, plain_ahead = gated_kernel_ms(torch, stream, step_plain, max(args.steps // 2, 3),
+                                               held_warm(settle(torch, step_plain, 0.05), 2))
     flops = p.flops
     nbytes = 2 * (p.m * p.k + p.k * p.n) + 2 * p.m * p.n
     kernel_s = mean_ms / 1e3
@@ -673,6 +689,7 @@ def run_splitk(args, torch, tg, profiling):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": settled,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -693,6 +710,7 @@ def run_splitk(args, torch, tg, profiling):
                      "kernel_ms_each_min": round(float(np.min(kms)), 5),
                      "kernel_ms_each_p90": round(float(np.percentile(kms, 90)), 5),
                      "launches_queued_ahead": bool(queued_ahead),
+                     "launches_warm_before_events": held_warm(settled, args.warmup),
                      "algorithmic": {"flops": flops, "bytes": nbytes}},
     }
     if not args.no_cpu_baseline:
@@ -760,6 +778,37 @@ def cpu_baseline_attention(p, seconds):
                       f"{p.d} terms, softmax, and a {p.n_k}-term weighted sum per output), {t:.1f} s on "
                       f"{threads} threads; all {p.batch * p.n_q} rows would take "
                       f"{t * p.batch * p.n_q / len(rows):.0f} s"}
+
+
+def settle(torch, step, seconds):
+    """Run the step back to back for about `seconds` (in batches that double,
+    one device synchronisation after each) and return what ran: after an
+    idle GPU the first ~100 launches of a large product are 4-19% slower than
+    the steady state (8192^3: ~860 us in launches 10-20 against ~766 from the
+    100th; O = P V: ~277 against ~233), while the clocks and the power
+    controller adjust.  The timed steps come after this and the warmup."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n, batch, el = 0, 1, 0.0
+    while el < seconds:
+        for _ in range(batch):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        batch = min(2 * batch, 4096)
+    return {"launches": n, "seconds": round(el, 4), "ms_per_launch": round(el * 1e3 / n, 5) if n else None}
+
+
+def held_warm(settled, warmup, seconds=0.1, cap=1000):
+    """Untimed steps queued ahead of the event-timed ones behind the GPU
+    sleep (the sleep lets the clocks drop again): about `seconds` of them,
+    at least the warmup count and 1, at most `cap` (the stream's queue holds
+    a bounded number of launches; past it the host waits for the GPU and the
+    queue no longer stays ahead)."""
+    per = settled.get("ms_per_launch") if settled else None
+    need = int(seconds * 1e3 / per) + 1 if per else 1
+    return max(warmup, 1, min(need, cap))
 
 
 def _held(torch, stream, enqueue):
