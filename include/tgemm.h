@@ -320,13 +320,15 @@ int32_t tg_splitk_choose(const gemm_plan_t* plan);
  * the product with V (round to nearest even), and O to out_type.
  * head_dim: 64 or 128.  scale: finite and > 0 (1/sqrt(head_dim) is the usual
  * choice).  Leading dims >= head_dim, < 2^20, multiples of 8; the four base
- * pointers 16-byte aligned and (batch > 1) the strides multiples of 8.
+ * pointers 16-byte aligned and (batch > 1) the strides multiples of 8; each
+ * head's K and V span under 2 GiB ((n_k - 1) * ld + head_dim < 2^30 elements).
  * Ownership: all pointers are caller-owned device memory; nothing is
  * allocated.  O must not alias Q, K or V; heads' outputs must not overlap.
  * Returns TG_OK (batch = 0 or n_q = 0 launches nothing), TG_ERR_INVALID
  * (negative size or stride, n_k = 0 with work to do, bad scale, leading dim
  * below head_dim, null pointer, overlapping outputs, offset overflow),
- * TG_ERR_UNSUPPORTED (dtype pair, head_dim, alignment, leading dim >= 2^20),
+ * TG_ERR_UNSUPPORTED (dtype pair, head_dim, alignment, leading dim >= 2^20,
+ * a head's K or V span of 2 GiB or more),
  * TG_ERR_HIP (launch failed).
  */
 tg_status attention_fwd(tg_dtype in_type, tg_dtype out_type, int64_t batch, int64_t n_q, int64_t n_k,

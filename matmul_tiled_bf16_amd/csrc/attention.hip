@@ -60,6 +60,10 @@ tg_status attention_fwd(tg_dtype in_type, tg_dtype out_type, int64_t batch, int6
   if (batch > 1 && stride_o < (n_q - 1) * ldo + head_dim) return TG_ERR_INVALID;  // heads' outputs overlap
   const int64_t lim = (int64_t)1 << 20;
   if (ldq >= lim || ldk >= lim || ldv >= lim || ldo >= lim) return TG_ERR_UNSUPPORTED;
+  // the kernel addresses a head's K and V through one buffer resource each,
+  // with 32-bit byte offsets
+  const int64_t span = (int64_t)1 << 30;
+  if ((n_k - 1) * ldk + head_dim >= span || (n_k - 1) * ldv + head_dim >= span) return TG_ERR_UNSUPPORTED;
   // 16-byte loads and stores along d
   const bool aligned = (uintptr_t)Q % 16 == 0 && (uintptr_t)K % 16 == 0 && (uintptr_t)V % 16 == 0 &&
                        (uintptr_t)O % 16 == 0 && ldq % 8 == 0 && ldk % 8 == 0 && ldv % 8 == 0 && ldo % 8 == 0 &&

@@ -143,21 +143,22 @@ __global__ void __launch_bounds__(512) attn_pp_kernel(AttnArgs a) {
     work_coords<1>(w0, total, a.q_blocks, 1, b, qb, unused);
     const int64_t q0 = (int64_t)qb * BM;
     const int64_t rows_q = min((int64_t)BM, a.n_q - q0);
-    const uint16_t* Kh = a.K + b * a.sk;
-    const uint16_t* Vh = a.V + b * a.sv;
+    // one resource per operand and head: rows at or past n_k lie past its
+    // size and read as zero (the launcher keeps each head's span below 2 GiB,
+    // so a block's byte offset rides in the 32-bit per-lane offset)
+    const i32x4 rk = make_rsrc(a.K + b * a.sk, ((a.n_k - 1) * a.ldk + D) * 2);
+    const i32x4 rv = make_rsrc(a.V + b * a.sv, ((a.n_k - 1) * a.ldv + D) * 2);
+    const uint32_t kstep = (uint32_t)(BN * a.ldk * 2), vstep = (uint32_t)(BN * a.ldv * 2);
 
     auto issue = [&](int32_t j) __attribute__((always_inline)) {
-      const int64_t k0 = (int64_t)j * BN;
-      const int64_t valid = min((int64_t)BN, a.n_k - k0);
-      const i32x4 rk = make_rsrc(Kh + k0 * a.ldk, ((valid - 1) * a.ldk + D) * 2);
-      const i32x4 rv = make_rsrc(Vh + k0 * a.ldv, ((valid - 1) * a.ldv + D) * 2);
       const uint32_t part = (uint32_t)(wave * PW) * 1024u;
       const uint32_t ks = lds0 + (uint32_t)(j % RK) * TILE + part;
       const uint32_t vs = lds0 + RK * TILE + (uint32_t)(j % RV) * TILE + part;
+      const uint32_t kb = (uint32_t)j * kstep, vb = (uint32_t)j * vstep;
 #pragma unroll
-      for (int i = 0; i < PW; ++i) dma16(rk, koff[i], ks + (uint32_t)i * 1024u);
+      for (int i = 0; i < PW; ++i) dma16(rk, koff[i] + kb, ks + (uint32_t)i * 1024u);
 #pragma unroll
-      for (int i = 0; i < PW; ++i) dma16(rv, voff[i], vs + (uint32_t)i * 1024u);
+      for (int i = 0; i < PW; ++i) dma16(rv, voff[i] + vb, vs + (uint32_t)i * 1024u);
     };
 
     // Q fragments of this lane's row: d = 16 ks + 8 lg .. +7 (loaded before
@@ -252,7 +253,10 @@ __global__ void __launch_bounds__(512) attn_pp_kernel(AttnArgs a) {
       if (i + 3 < nkb) issue(i + 3);
       if (ragged && i == nkb - 1) {
         asm volatile("" ::: "memory");
-        const int thr = (int)(a.n_k - (int64_t)i * BN) - 4 * lg;
+        // opaque, so that the compare masks are not hoisted out of the loop
+        // into scalar registers
+        int thr = (int)(a.n_k - (int64_t)i * BN) - 4 * lg;
+        asm volatile("" : "+v"(thr));
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -264,10 +268,12 @@ __global__ void __launch_bounds__(512) attn_pp_kernel(AttnArgs a) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mxs = mx * a.c;
-      if (__builtin_amdgcn_ballot_w64(mxs > m + TAU)) {
+      // A row's maximum exceeds m + TAU exactly when one of its two lanes'
+      // halves does (scaling by c > 0 keeps the order), so the lanes decide
+      // on their own halves and meet their partner only when m is raised.
+      if (__builtin_amdgcn_ballot_w64(mx * a.c > m + TAU)) {
         asm volatile("" ::: "memory");  // a branch, not 64 multiplies per block
+        const float mxs = fmaxf(mx, __shfl_xor(mx, 32)) * a.c;
         const float mn = fmaxf(m, mxs);
         const float alpha = __builtin_amdgcn_exp2f(m - mn);
         m = mn;
