@@ -325,6 +325,8 @@ def attn_call(**kw):
     (dict(ldk=132), tg.TG_ERR_UNSUPPORTED),            # not a multiple of 8
     (dict(V=4096 + 2), tg.TG_ERR_UNSUPPORTED),         # misaligned base
     (dict(ldq=1 << 20, sq=256 << 20), tg.TG_ERR_UNSUPPORTED),
+    (dict(n_k=1 << 23, sk=128 << 23, sv=128 << 23), tg.TG_ERR_UNSUPPORTED),   # a head's K spans 2 GiB
+    (dict(n_k=1 << 22, ldv=512, sv=512 << 22), tg.TG_ERR_UNSUPPORTED),       # a head's V spans 2 GiB
     (dict(batch=0, Q=None, K=None, V=None, O=None), tg.TG_OK),   # nothing to do
     (dict(n_q=0, n_k=0, O=None), tg.TG_OK),
 ])
