@@ -378,9 +378,9 @@ def run_configs(torch, tg, profiling):
             # small products are measured hot (their operands stay in the caches, as they
             # would between back-to-back calls); large HBM-bound ones from HBM
             small = p.name.startswith(("square_256", "ragged_1000"))
+            # (S = Q K^T too: its 2 GiB output is stored non-temporally, so a single
+            # copy of its 64 MiB operands could stay in the Infinity Cache)
             copies = 4 if bound == "hbm" and not small else 1
-            if p.name.startswith("attn_s"):
-                copies = 1  # 2 GiB of output per launch: nothing of it stays in a cache
             A0, B0 = up(p.A), up(p.B)
             As = [A0] + [A0.clone() for _ in range(copies - 1)] if big_a else [A0]
             Bs = [B0] + [B0.clone() for _ in range(copies - 1)] if not big_a else [B0]
