@@ -108,7 +108,8 @@ int skinny_choose(int64_t m, int64_t) { return m > 16 ? 1 : 0; }
 //  * HBM-bound ones with K <= 128 and >= 2048 tiles take the panel kernel
 //    (runs of 128x128 tiles along a row panel of C: the next tile's B copy
 //    overlaps this tile's stores);
-//  * other HBM-bound ones take 128x128 tiles, two work-groups per CU, whose
+//  * other HBM-bound ones take 256x128 tiles when N <= 256 (B panels read
+//    half as often), else 128x128 tiles, two work-groups per CU, whose
 //    operand panels and 1 KiB row-segment stores keep the streams long;
 //  * small and ragged problems take 64x64 tiles so that there are at least
 //    ~256 work-groups, with a 4-deep ring when K is long.
@@ -128,6 +129,11 @@ int choose_tile(const gemm_plan_t& p, int64_t batch) {
   if (mfma_bound && items(tg::kWideTile) > 128 && k > 0) return tg::kPingPongTile;
   // short K and many tiles: runs along row panels, A held in registers
   if (!mfma_bound && panel_ok(p) && items(tg::kPanelTile) >= 2048) return tg::kPanelTile;
+  // HBM-bound with N <= 256: 256x128 tiles read each B panel half as often
+  // as 128-row ones (128 x 2048x128x2048, fp32 out: 226 -> 205 us; 128 x
+  // 512x128x8192: 286 -> 223 us; N = 64: 219 -> 201 us).  They need enough
+  // work items (16384x128x16384, 64 of them: 229 -> 276 us) and rows.
+  if (!mfma_bound && n <= 256 && m >= 256 && items(tg::kTallTile) >= 256) return tg::kTallTile;
   // 128x128, two work-groups per CU: HBM-bound products, and MFMA-bound ones
   // below the ping-pong kernel's range (measured faster than one work-group
   // per CU on every such shape tried: 1536x3072x8192 105 vs 173 us, 2560^2 x

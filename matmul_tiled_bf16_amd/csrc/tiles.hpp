@@ -62,13 +62,16 @@ constexpr TileShape kTiles[] = {
     {64, 64, 64, 2, 2, 2, 1, 0, kTileEpi},      // 13: twin of 0, 2, 11
     {128, 128, 64, 2, 2, 2, 1, 0, kTileEpi},    // 14: twin of 1, 5, 6, 7
     {256, 256, 32, 2, 4, 4, 1, 0, kTileEpi},    // 15: twin of 3
-    {128, 128, 64, 2, 2, 2, 2, 0, kTileEpi},    // 16: twin of 4
+    {128, 128, 64, 2, 2, 2, 2, 0, kTileEpi},    // 16: twin of 4 and 17
+    // 256x128, 8 waves of 64x64 each, one work-group per CU (96 KiB): HBM-bound
+    // products with N <= 256, whose B panels 128-row tiles read twice as often
+    {256, 128, 64, 4, 2, 2, 1},  // 17
 };
 constexpr int kSmallTile = 0, kMfmaMidTile = 1, kThinTile = 2, kWideTile = 3, kHbmTile = 4, kDeepSmallTile = 11;
-constexpr int kKSliceTile = 12;
+constexpr int kKSliceTile = 12, kTallTile = 17;
 // the epilogue twin of a tile-kernel entry
 constexpr int epi_twin(int t) {
-  return t == 3 ? 15 : t == 4 ? 16 : (t == 1 || t == 5 || t == 6 || t == 7) ? 14 : 13;
+  return t == 3 ? 15 : (t == 4 || t == 17) ? 16 : (t == 1 || t == 5 || t == 6 || t == 7) ? 14 : 13;
 }
 constexpr int kPingPongTile = 8, kPingPongEpiTile = 9, kPanelTile = 10;
 constexpr int kPanelKMax = kTiles[kPanelTile].bk;  // the panel kernel holds all of K at once

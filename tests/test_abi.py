@@ -164,11 +164,11 @@ def test_plan_choices_for_the_workloads():
     assert p.variant == tg.VARIANT_TILE and p.flags & tg.FLAG_EVEN_K
     p = tg.plan(2048, 128, 2048)
     assert p.variant == tg.VARIANT_TILE
-    # batched attention shapes, planned for their batch of 128: 128x128 tiles (HBM-bound), and the
-    # single-column O = P V rotates its K walks
+    # batched attention shapes, planned for their batch of 128 (HBM-bound): 128x128 tiles for S,
+    # 256x128 for the single-column O = P V, which rotates its K walks
     for mm, nn, kk, tb in [(2048, 2048, 128, True), (2048, 128, 2048, False)]:
         p = tg.plan(mm, nn, kk, trans_b=tb, batch=128)
-        assert (p.variant, p.bm, p.bn) == (tg.VARIANT_TILE, 128, 128)
+        assert (p.variant, p.bm, p.bn) == (tg.VARIANT_TILE, 256 if nn == 128 else 128, 128)
         assert bool(p.flags & tg.FLAG_ROTATE_K) == (nn == 128)
         assert p.flags & tg.FLAG_PERSIST and not p.flags & tg.FLAG_PREFETCH  # HBM-bound: LDS-staged stores
         assert p.flags & tg.FLAG_STREAM_C  # outputs of 128 MiB and 2 GiB: non-temporal stores
@@ -181,7 +181,10 @@ def test_plan_choices_for_the_workloads():
     assert tg.plan(2048, 2048, 128, trans_a=True, trans_b=True, batch=128).tile == 4
     assert tg.plan(2048, 2048, 136, trans_b=True, batch=128).tile == 4
     assert tg.plan(2048, 2048, 128, trans_b=True).tile == 4
-    assert tg.plan(2048, 128, 2048, batch=128).tile == 4
+    assert tg.plan(2048, 128, 2048, batch=128).tile == 17                      # N <= 256: 256 x 128
+    assert tg.plan(2048, 64, 2048, batch=128, out_dtype=torch.bfloat16).tile == 17
+    assert tg.plan(16384, 128, 16384).tile != 17                                # 64 of its items
+    assert tg.plan(2048, 512, 2048, batch=128).tile == 4                        # N > 256
     with pytest.raises(tg.TgError):
         tg.plan(64, 64, 64, batch=0)
     p = tg.plan(8192, 8192, 8192, out_dtype=torch.bfloat16)
