@@ -144,3 +144,12 @@ def test_epilogue_misaligned_bias_rejected():
     e = tg.Epilogue(1.0, 0.0, bias.data_ptr() + 2)
     st = tg.lib().gemm_run_ex(ctypes.byref(pl), ctypes.byref(e), A.data_ptr(), A.data_ptr(), C.data_ptr(), None)
     assert st == tg.TG_ERR_INVALID
+
+
+@pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
+def test_epilogue_on_a_256x128_plan(out_dtype):
+    """An O = P V shaped batch (HBM-bound, N = 128, 256 work items) is planned
+    onto the 256 x 128 entry; with an epilogue the launcher sends it to the
+    128 x 128 epilogue twin.  Integer data: bit for bit."""
+    pl = run(512, 128, 128, 0, 0, out_dtype, 2.0, -1.0, True, seed=18, dist=("int", -3, 3), batch=128, exact=True)
+    assert (pl.variant, pl.tile, pl.bm, pl.bn) == (tg.VARIANT_TILE, 17, 256, 128)
